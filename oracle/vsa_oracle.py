@@ -1,0 +1,343 @@
+"""CPU oracle for tile-sparse video attention.
+
+TEST INFRASTRUCTURE ONLY. This module exists to check the HIP library; it is
+not part of the product path. Only the test suite, the package's smoke check
+and the benchmark's CPU-baseline leg may import or call it. It shares no code
+with the HIP path and imports nothing from it.
+
+Everything is plain NumPy in float64 (scores are additionally rounded to
+float32, because that is the precision the ranking is taken in). Each
+function follows one step of the method as the pages describe it, in their
+order, with the pages' notation where they have one:
+
+  1. tile map          segment-pure prefix tiles, then 3D video tiles
+  2. gather            tokens into tile-major order, pads are zero
+  3. pool              mean-pool through a gate (VSA) or Avg/Max/Min TripPool
+  4. score             dot products of pooled tile descriptors
+  5. select            top-k video key tiles per video query tile
+  6. mask              prefix keys and prefix query rows always dense
+  7. attention         softmax attention over the allowed real keys
+
+Where the pages leave a step open, the reading taken is stated in the
+function's docstring (the full list of readings is in the design notes).
+
+Pins (what checks this oracle against something other than itself) live in
+tests/test_oracle_*.py: brute-force enumeration of the map, closed forms of
+pooling and attention, an O(n^2) rank definition for selection and
+torch's scaled_dot_product_attention with an explicit mask in float64.
+Parity unpinned against the pages themselves: they print no worked example,
+only the property that keeping 100% of tiles reproduces dense attention
+("BSAI-ComfyUI-VedaSparse" README, section "正确性验证 / Correctness").
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+TILE = 64  # tokens per tile ("From 650 s to 72 s", section "The method": 4x4x4 = 64)
+
+
+# --------------------------------------------------------------------------
+# 1. Tile map
+# --------------------------------------------------------------------------
+
+@dataclass
+class TileMap:
+    slot_to_token: np.ndarray   # int64 [n_tiles * 64]; -1 marks a pad slot
+    n_prefix_tiles: int
+    n_video_tiles: int
+    video_grid: tuple           # (nt, nh, nw) tiles per axis
+
+    @property
+    def n_tiles(self) -> int:
+        return self.n_prefix_tiles + self.n_video_tiles
+
+    def tile_tokens(self, tile: int) -> np.ndarray:
+        """Real token indices of one tile, in slot order."""
+        s = self.slot_to_token[tile * TILE:(tile + 1) * TILE]
+        return s[s >= 0]
+
+    def valid(self) -> np.ndarray:
+        """bool [n_tiles, 64]: slot holds a real token."""
+        return (self.slot_to_token >= 0).reshape(self.n_tiles, TILE)
+
+
+def tile_map(T: int, Hv: int, Wv: int, prefix, shape) -> TileMap:
+    """Token -> tile layout for one head shape.
+
+    Prefix segments (text, reference image, reference audio, in the caller's
+    sequence order) each get their own tiles so no tile mixes modalities
+    ("Ref2VA VSA" node news, section "Патч внимания с двумя уровнями",
+    item 1; ComfyUI-Ref2VA-VSA README, "Multimodal Dense-Exempt Prefix").
+    Segment s with offset o_s and length L_s fills ceil(L_s / 64) tiles;
+    slot j holds token o_s + j while j < L_s and is a pad after that.
+
+    Video tokens follow the prefix, row-major in (t, y, x). They are grouped
+    in 3D tiles of (pt, ph, pw) = ``shape`` with pt*ph*pw = 64: 4x4x4 for VSA
+    ("From 650 s to 72 s", section "The method"), any per-head shape for
+    Veda ("BSAI-ComfyUI-VedaSparse" README, Overview table, Head-Aware
+    Tiling). Reading: each axis is padded up to a multiple of the tile edge;
+    video tile (ti, hi, wi) is tile n_prefix_tiles + (ti*nh + hi)*nw + wi, and
+    slot (a*ph + b)*pw + c holds position (ti*pt + a, hi*ph + b, wi*pw + c),
+    or a pad when that falls outside the grid.
+    """
+    pt, ph, pw = (int(s) for s in shape)
+    assert pt * ph * pw == TILE, "tile shape must hold 64 tokens"
+    slots = []
+    offset = 0
+    n_prefix_tiles = 0
+    for L in prefix:
+        L = int(L)
+        n = -(-L // TILE)
+        j = np.arange(n * TILE)
+        slots.append(np.where(j < L, offset + j, -1))
+        offset += L
+        n_prefix_tiles += n
+    P = offset
+    nt, nh, nw = -(-T // pt), -(-Hv // ph), -(-Wv // pw)
+    ti, hi, wi, a, b, c = np.meshgrid(np.arange(nt), np.arange(nh), np.arange(nw),
+                                      np.arange(pt), np.arange(ph), np.arange(pw),
+                                      indexing="ij")
+    t, y, x = ti * pt + a, hi * ph + b, wi * pw + c
+    inside = (t < T) & (y < Hv) & (x < Wv)
+    video = np.where(inside, P + (t * Hv + y) * Wv + x, -1).reshape(-1)
+    slots.append(video)
+    s2t = np.concatenate(slots).astype(np.int64)
+    return TileMap(s2t, n_prefix_tiles, nt * nh * nw, (nt, nh, nw))
+
+
+# --------------------------------------------------------------------------
+# 2. Gather
+# --------------------------------------------------------------------------
+
+def gather(x: np.ndarray, tmap: TileMap) -> np.ndarray:
+    """[N, d] token rows -> [n_tiles, 64, d] tile-major rows; pads are zero.
+
+    The whole-tile row gather of the memory-bounded engine
+    ("BSAI-ComfyUI-VedaSparse" README, section "六、实现说明 / Implementation").
+    """
+    s2t = tmap.slot_to_token
+    out = np.zeros((s2t.size, x.shape[1]), dtype=x.dtype)
+    real = s2t >= 0
+    out[real] = x[s2t[real]]
+    return out.reshape(tmap.n_tiles, TILE, x.shape[1])
+
+
+# --------------------------------------------------------------------------
+# 3. Pool
+# --------------------------------------------------------------------------
+
+def _video_part(xt: np.ndarray, tmap: TileMap):
+    v = tmap.valid()[tmap.n_prefix_tiles:]
+    return np.asarray(xt[tmap.n_prefix_tiles:], dtype=np.float64), v
+
+
+def pool_mean_gate(xt: np.ndarray, tmap: TileMap, gate: np.ndarray) -> np.ndarray:
+    """VSA tile descriptor: mean of a video tile's real rows, times the gate.
+
+    The gating projection to_gate_compress decides which tiles a query tile
+    attends to ("From 650 s to 72 s", section "The method"). Reading: the
+    same per-head d x d gate multiplies the pooled Q tile and the pooled K
+    tile; pad slots are left out of the mean. Returns float64 [n_video, r].
+    """
+    x, v = _video_part(xt, tmap)
+    counts = v.sum(axis=1).astype(np.float64)
+    mean = (x * v[:, :, None]).sum(axis=1) / counts[:, None]
+    return mean @ np.asarray(gate, dtype=np.float64)
+
+
+def pool_trippool(xt: np.ndarray, tmap: TileMap, proj: np.ndarray) -> np.ndarray:
+    """Veda TripPool tile descriptor: [Avg, Max, Min] of projected tokens.
+
+    Each real token of a video tile is projected by the head's d x r matrix,
+    then the channel-wise mean, maximum and minimum over the tile's real
+    tokens are concatenated ("BSAI-ComfyUI-VedaSparse" README, Overview table,
+    TripPool row: Avg, Max and Min statistics per tile; Implementation
+    section, the TripPool descriptor). Reading: project first, pool after;
+    pads are left out. Returns float64 [n_video, 3r].
+    """
+    x, v = _video_part(xt, tmap)
+    y = x @ np.asarray(proj, dtype=np.float64)            # [n_video, 64, r]
+    counts = v.sum(axis=1).astype(np.float64)
+    m = v[:, :, None]
+    avg = np.where(m, y, 0.0).sum(axis=1) / counts[:, None]
+    mx = np.where(m, y, -np.inf).max(axis=1)
+    mn = np.where(m, y, np.inf).min(axis=1)
+    return np.concatenate([avg, mx, mn], axis=1)
+
+
+# --------------------------------------------------------------------------
+# 4. Score
+# --------------------------------------------------------------------------
+
+def tile_scores(qhat: np.ndarray, khat: np.ndarray) -> np.ndarray:
+    """s[i, j] = qhat_i . khat_j for video query tile i and video key tile j.
+
+    Plain dot product of the tile descriptors, as the heuristic scorer with
+    the identity (unit) projection does ("BSAI-ComfyUI-VedaSparse" README,
+    scorer modes table, heuristic row). Reading: no 1/sqrt(d) and no softmax
+    over tiles, since neither changes the order. Computed in float64 and
+    rounded to float32, the precision the ranking uses. Prefix tiles are
+    never scored: they are always kept.
+    """
+    s = np.asarray(qhat, dtype=np.float64) @ np.asarray(khat, dtype=np.float64).T
+    return s.astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# 5. Select
+# --------------------------------------------------------------------------
+
+def keep_count(sparsity: float, n_video_tiles: int) -> int:
+    """k = number of video key tiles kept per video query tile.
+
+    "75% sparsity" keeps the top 25% of tiles ("From 650 s to 72 s", section
+    "Where the time went"). Reading: the kept share is fixed once as integer
+    basis points, keep_bp = round_half_up((1 - sparsity) * 10^4), and
+    k = max(1, ceil(keep_bp * n / 10^4)) in integer arithmetic, so that
+    e.g. 5% of 3780 tiles is exactly 189.
+    """
+    keep_bp = int(math.floor((1.0 - float(sparsity)) * 10000.0 + 0.5))
+    return max(1, -(-(keep_bp * int(n_video_tiles)) // 10000))
+
+
+def select_topk(scores: np.ndarray, k: int) -> np.ndarray:
+    """Top-k key tiles per query tile, as ascending index lists.
+
+    Each video query tile keeps its k best-scoring video key tiles
+    ("Ref2VA VSA" node news, item 2: top-k pruning applies to generated-video
+    key tiles only; "Veda Sparse Attention в ComfyUI", section "Что делает
+    Veda": head-aware top-k forms the tile mask). Order: higher score first,
+    the lower tile index first among equal scores, i.e. tile j is kept iff
+    #{j' : s_j' > s_j} + #{j' < j : s_j' = s_j} < k. A stable sort (a library
+    primitive) realises that order. Returns int64 [n_query, k], each row
+    ascending.
+    """
+    s = np.asarray(scores, dtype=np.float32)
+    n = s.shape[1]
+    idx = np.arange(n)
+    out = np.empty((s.shape[0], k), dtype=np.int64)
+    for i in range(s.shape[0]):
+        order = np.lexsort((idx, -s[i]))
+        out[i] = np.sort(order[:k])
+    return out
+
+
+# --------------------------------------------------------------------------
+# 6. Mask
+# --------------------------------------------------------------------------
+
+def allowed_tiles(tmap: TileMap, kv_video) -> np.ndarray:
+    """bool [n_tiles, n_tiles]: query tile may attend to key tile.
+
+    Prefix key tiles are never pruned ("Ref2VA VSA" node news, item 1) and
+    prefix (conditioning) query rows stay exact, i.e. attend to everything
+    ("BSAI-ComfyUI-VedaSparse" README, v3.4 highlights: conditioning rows
+    always dense, sink = exact_kv_and_rows). A video query tile attends to
+    all prefix tiles plus its selected video key tiles. ``kv_video`` holds,
+    per video query tile, video-local key tile indices.
+    """
+    npf, n = tmap.n_prefix_tiles, tmap.n_tiles
+    allow = np.zeros((n, n), dtype=bool)
+    allow[:npf, :] = True
+    allow[:, :npf] = True
+    for i, row in enumerate(kv_video):
+        allow[npf + i, npf + np.asarray(row, dtype=np.int64)] = True
+    return allow
+
+
+# --------------------------------------------------------------------------
+# 7. Attention
+# --------------------------------------------------------------------------
+
+def softmax_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float):
+    """Rows of softmax(q k^T * scale) v over the given keys, and their LSE.
+
+    Subtract the row maximum, exponentiate, normalise. float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    logits = (q @ k.T) * scale
+    mx = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - mx)
+    den = e.sum(axis=1, keepdims=True)
+    out = (e @ v) / den
+    lse = (mx + np.log(den))[:, 0]
+    return out, lse
+
+
+def sparse_attention(q, k, v, tmap: TileMap, allow: np.ndarray, scale: float,
+                     query_tiles=None):
+    """Tile-skipping attention: each query tile sees only its allowed tiles.
+
+    Each query tile attends exactly to the key tiles it keeps and skips the
+    rest ("Veda Sparse Attention в ComfyUI", section "Что делает Veda";
+    "BSAI-ComfyUI-VedaSparse" README, Tile-Skipping row). Pad slots are
+    neither queries nor keys. The result for a query token is written at the
+    token's own sequence position. Rows of tiles not in ``query_tiles`` stay
+    NaN. Returns (out [N, d], lse [N]) in float64.
+    """
+    N, d = q.shape
+    out = np.full((N, v.shape[1]), np.nan)
+    lse = np.full(N, np.nan)
+    tiles = range(tmap.n_tiles) if query_tiles is None else query_tiles
+    for tq in tiles:
+        rows = tmap.tile_tokens(tq)
+        if rows.size == 0:
+            continue
+        keys = np.concatenate([tmap.tile_tokens(tk)
+                               for tk in np.nonzero(allow[tq])[0]])
+        o, l = softmax_attention(q[rows], k[keys], v[keys], scale)
+        out[rows] = o
+        lse[rows] = l
+    return out, lse
+
+
+def dense_attention(q, k, v, scale: float):
+    """Full softmax attention of every token over every token (float64)."""
+    return softmax_attention(q, k, v, scale)
+
+
+def effective_flops(tmap: TileMap, allow: np.ndarray, d: int) -> int:
+    """4*d * sum over query tiles of (real queries) x (real allowed keys).
+
+    QK^T and PV, two flops per multiply-add; softmax not counted.
+    """
+    real = tmap.valid().sum(axis=1).astype(np.int64)
+    keys = allow.astype(np.int64) @ real
+    return int(4 * d * int((real * keys).sum()))
+
+
+# --------------------------------------------------------------------------
+# The whole path for one (batch, head)
+# --------------------------------------------------------------------------
+
+def head_forward(q, k, v, grid, prefix, shape, sparsity, scorer, wq, wk=None,
+                 scale=None, query_tiles=None, kv_video=None):
+    """Map -> gather -> pool -> score -> select -> attention for one head.
+
+    ``scorer`` is "mean_gate" (``wq`` is the gate; ``wk`` defaults to it) or
+    "trippool" (``wq``, ``wk`` are the per-head projections). ``kv_video``
+    overrides the selection (a caller-supplied valid selection). Returns a
+    dict with every intermediate.
+    """
+    T, Hv, Wv = grid
+    d = q.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    tmap = tile_map(T, Hv, Wv, prefix, shape)
+    qt, kt = gather(q, tmap), gather(k, tmap)
+    wk = wq if wk is None else wk
+    pool = pool_mean_gate if scorer == "mean_gate" else pool_trippool
+    qhat, khat = pool(qt, tmap, wq), pool(kt, tmap, wk)
+    scores = tile_scores(qhat, khat)
+    kk = keep_count(sparsity, tmap.n_video_tiles)
+    sel = select_topk(scores, kk) if kv_video is None else np.asarray(kv_video)
+    allow = allowed_tiles(tmap, sel)
+    out, lse = sparse_attention(q, k, v, tmap, allow, scale, query_tiles)
+    return {"tmap": tmap, "qt": qt, "kt": kt, "qhat": qhat, "khat": khat,
+            "scores": scores, "k": kk, "kv_video": sel, "allow": allow,
+            "out": out, "lse": lse}

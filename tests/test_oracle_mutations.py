@@ -1,0 +1,109 @@
+"""Planted mistakes in the oracle must trip its pins (CPU only).
+
+Each case swaps one oracle step for a plausibly wrong variant (a transposed
+axis, a dropped mask, a wrong tie rule, a missing scale ...) and checks that
+at least one pin test fails on it. The oracle itself is untouched outside
+the monkeypatched scope.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.vsa_oracle as vo
+from tests import test_oracle_attention as ta
+from tests import test_oracle_map as tm_
+from tests import test_oracle_pool_score as tp
+from tests import test_oracle_select as ts
+
+
+def _map_swapped_xy(T, Hv, Wv, prefix, shape):
+    return _orig_tile_map(T, Wv, Hv, prefix, shape)   # wrong axis order
+
+
+def _map_prefix_shared(T, Hv, Wv, prefix, shape):
+    # all prefix segments packed together (modalities share tiles)
+    return _orig_tile_map(T, Hv, Wv, (sum(prefix),) if prefix else (), shape)
+
+
+def _pool_mean_with_pads(xt, tmap, gate):
+    x, v = vo._video_part(xt, tmap)
+    return x.mean(axis=1) @ np.asarray(gate, dtype=np.float64)
+
+
+def _trippool_wrong_order(xt, tmap, proj):
+    r = np.asarray(proj).shape[1]
+    p = _orig_trippool(xt, tmap, proj)
+    return np.concatenate([p[:, r:2 * r], p[:, :r], p[:, 2 * r:]], axis=1)
+
+
+def _scores_transposed(qhat, khat):
+    return _orig_scores(qhat, khat).T.copy()
+
+
+def _select_high_index_ties(scores, k):
+    s = np.asarray(scores, dtype=np.float32)
+    out = np.empty((s.shape[0], k), dtype=np.int64)
+    for i in range(s.shape[0]):
+        order = np.lexsort((-np.arange(s.shape[1]), -s[i]))
+        out[i] = np.sort(order[:k])
+    return out
+
+
+def _keep_count_float_ceil(sparsity, n):
+    return max(1, int(math.ceil((1.0 - sparsity) * n)))
+
+
+def _softmax_no_scale(q, k, v, scale):
+    return _orig_softmax(q, k, v, 1.0)
+
+
+def _allowed_no_prefix_rows(tmap, kv_video):
+    a = _orig_allowed(tmap, kv_video)
+    a[:tmap.n_prefix_tiles, tmap.n_prefix_tiles:] = False
+    return a
+
+
+_orig_tile_map = vo.tile_map
+_orig_trippool = vo.pool_trippool
+_orig_scores = vo.tile_scores
+_orig_softmax = vo.softmax_attention
+_orig_allowed = vo.allowed_tiles
+
+GEOM = tm_.GEOMS[1]
+
+
+def _run_map_pin():
+    tm_.test_map_matches_token_to_slot_enumeration(*GEOM)
+
+
+def _run_prefix_pin():
+    tm_.test_prefix_tiles_are_segment_pure(*tm_.GEOMS[0])
+
+
+CASES = [
+    ("tile_map", _map_swapped_xy, _run_map_pin),
+    ("tile_map", _map_prefix_shared, _run_prefix_pin),
+    ("pool_mean_gate", _pool_mean_with_pads, tp.test_mean_gate_constant_tile_closed_form),
+    ("pool_trippool", _trippool_wrong_order, tp.test_trippool_order_and_values_by_hand),
+    ("tile_scores", _scores_transposed, tp.test_scores_direct_formula_and_orientation),
+    ("select_topk", _select_high_index_ties, ts.test_ties_go_to_lower_index_and_signed_zero_ties),
+    ("keep_count", _keep_count_float_ceil, ts.test_keep_count_exact_where_float_ceil_is_not),
+    ("softmax_attention", _softmax_no_scale, ta.test_full_keep_equals_dense),
+    ("allowed_tiles", _allowed_no_prefix_rows,
+     lambda: ta.test_prefix_rows_are_dense_at_any_sparsity(0.75)),
+]
+
+
+@pytest.mark.parametrize("name,bad,pin", CASES, ids=[c[0] + "-" + c[1].__name__ for c in CASES])
+def test_planted_mistake_is_caught(monkeypatch, name, bad, pin):
+    monkeypatch.setattr(vo, name, bad)
+    monkeypatch.setattr(oracle, name, bad)
+    with pytest.raises(AssertionError):
+        pin()
+
+
+@pytest.mark.parametrize("name,bad,pin", CASES[:1], ids=["sanity"])
+def test_pins_pass_on_the_real_oracle(name, bad, pin):
+    pin()
