@@ -1,0 +1,34 @@
+// Host planner: the validated problem with every derived count. The struct is
+// trivially copyable and is handed to every kernel by value.
+#pragma once
+
+#include <stdint.h>
+
+#include "vsa.h"
+
+struct Plan {
+  int32_t B, H, N, d, T, Hv, Wv;
+  int32_t dtype;
+  int32_t n_prefix;
+  int32_t prefix_len[VSA_MAX_SEGMENTS];
+  int32_t prefix_off[VSA_MAX_SEGMENTS];        // first token of the segment
+  int32_t prefix_tile0[VSA_MAX_SEGMENTS + 1];  // first tile of the segment
+  int32_t P;                                   // prefix tokens
+  int32_t n_shapes;
+  int32_t shape[VSA_MAX_SHAPES][3];            // (pt, ph, pw)
+  int32_t grid_t[VSA_MAX_SHAPES], grid_h[VSA_MAX_SHAPES], grid_w[VSA_MAX_SHAPES];
+  int32_t n_prefix_tiles;
+  int32_t n_tiles[VSA_MAX_SHAPES];
+  int32_t n_vt[VSA_MAX_SHAPES];
+  int32_t k[VSA_MAX_SHAPES];
+  int32_t max_tiles, max_vt, k_max, keep_bp;
+  int32_t dense;                               // sparsity == 0
+  int64_t tiles_per_batch;                     // sum over heads of n_tiles
+  int64_t tiles_per_cycle;                     // sum over one shape cycle
+};
+
+// Validates `prob` and fills `plan`. Returns a vsa_status. Host only.
+int make_plan(const vsa_problem *prob, double sparsity, Plan *plan);
+
+// Validates `prob` ignoring sparsity (steps that do not depend on it).
+int make_plan_geometry(const vsa_problem *prob, Plan *plan);

@@ -1,0 +1,315 @@
+"""Thin ctypes binding of libvsa.so (include/vsa.h), same names as the C ABI.
+
+Only argument marshalling lives here: shapes and dtypes are checked, torch
+tensors provide device memory, and the current torch stream is passed as the
+hipStream_t. Every step of the computation runs in the library's kernels.
+There is no fallback: if libvsa.so is missing the import of the library
+raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libvsa.so")
+
+VSA_OK, VSA_ERR_INVALID_ARG, VSA_ERR_UNSUPPORTED, VSA_ERR_SIZE, VSA_ERR_HIP = 0, -1, -2, -3, -4
+VSA_F32, VSA_BF16 = 0, 1
+VSA_SCORE_MEAN_GATE, VSA_SCORE_TRIPPOOL = 0, 1
+VSA_TILE, VSA_MAX_SEGMENTS, VSA_MAX_SHAPES = 64, 8, 16
+VSA_MAX_VIDEO_TILES, VSA_MAX_PROJ = 8192, 64
+
+# Names declared in include/vsa.h.
+EXPORTS = ("vsa_query_sizes", "vsa_pooled_bytes", "vsa_map_tiles", "vsa_tile_scores",
+           "vsa_select_topk", "vsa_sparse_attn_fwd", "vsa_kept_stats",
+           "vsa_count_flops", "vsa_status_string", "vsa_version")
+
+
+class vsa_problem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("T", ctypes.c_int32), ("Hv", ctypes.c_int32),
+                ("Wv", ctypes.c_int32), ("n_prefix", ctypes.c_int32),
+                ("prefix_len", ctypes.c_int32 * VSA_MAX_SEGMENTS),
+                ("n_shapes", ctypes.c_int32),
+                ("tile_shape", ctypes.POINTER(ctypes.c_int32)),
+                ("dtype", ctypes.c_int32)]
+
+
+class vsa_sizes(ctypes.Structure):
+    _fields_ = [("map_elems", ctypes.c_int64), ("tiled_elems", ctypes.c_int64),
+                ("pooled_rows", ctypes.c_int64), ("score_elems", ctypes.c_int64),
+                ("idx_elems", ctypes.c_int64), ("out_elems", ctypes.c_int64),
+                ("n_prefix_tiles", ctypes.c_int32), ("max_tiles", ctypes.c_int32),
+                ("max_video_tiles", ctypes.c_int32), ("k_max", ctypes.c_int32),
+                ("keep_bp", ctypes.c_int32),
+                ("n_tiles", ctypes.c_int32 * VSA_MAX_SHAPES),
+                ("n_video_tiles", ctypes.c_int32 * VSA_MAX_SHAPES),
+                ("k", ctypes.c_int32 * VSA_MAX_SHAPES)]
+
+
+class VSAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status} ({status_string(status)})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libvsa.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m block_sparse_video_map_amd.build` (no fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, S = ctypes.POINTER(vsa_problem), ctypes.POINTER(vsa_sizes)
+        vp, i32, i64, f64, f32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                  ctypes.c_double, ctypes.c_float)
+        sig = {
+            "vsa_query_sizes": [P, f64, S],
+            "vsa_pooled_bytes": [P, i32, i32, ctypes.POINTER(i64)],
+            "vsa_map_tiles": [P, vp, vp, vp, vp, vp, vp, vp, vp],
+            "vsa_tile_scores": [P, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp],
+            "vsa_select_topk": [P, vp, f64, vp, vp],
+            "vsa_sparse_attn_fwd": [P, vp, vp, vp, vp, vp, f64, f32, vp, vp, vp],
+            "vsa_kept_stats": [P, f64, ctypes.POINTER(i64), ctypes.POINTER(f64)],
+            "vsa_count_flops": [P, f64, vp, vp, ctypes.POINTER(f64)],
+            "vsa_status_string": [ctypes.c_int],
+            "vsa_version": [],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_char_p if name == "vsa_status_string" else ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().vsa_status_string(int(status)).decode()
+
+
+def vsa_version() -> int:
+    return lib().vsa_version()
+
+
+def _check(fn: str, status: int):
+    if status != VSA_OK:
+        raise VSAError(fn, status)
+
+
+@dataclass
+class Problem:
+    """Geometry of one attention layer (mirrors vsa_problem)."""
+    B: int
+    H: int
+    d: int
+    grid: Tuple[int, int, int]
+    prefix: Sequence[int]
+    tile_shapes: Sequence[Tuple[int, int, int]]
+    dtype: str = "bf16"         # "bf16" or "f32"
+    N: Optional[int] = None     # defaults to sum(prefix) + T*Hv*Wv
+
+    def __post_init__(self):
+        self.prefix = tuple(int(x) for x in self.prefix)
+        self.tile_shapes = tuple(tuple(int(v) for v in s) for s in self.tile_shapes)
+        if self.N is None:
+            T, Hv, Wv = self.grid
+            self.N = sum(self.prefix) + T * Hv * Wv
+        if len(self.prefix) > VSA_MAX_SEGMENTS or len(self.tile_shapes) > VSA_MAX_SHAPES:
+            raise ValueError("too many prefix segments or tile shapes")
+        flat = [v for s in self.tile_shapes for v in s]
+        self._shape_arr = (ctypes.c_int32 * max(1, len(flat)))(*flat)
+        st = vsa_problem()
+        st.B, st.H, st.N, st.d = self.B, self.H, self.N, self.d
+        st.T, st.Hv, st.Wv = self.grid
+        st.n_prefix = len(self.prefix)
+        for i, L in enumerate(self.prefix):
+            st.prefix_len[i] = L
+        st.n_shapes = len(self.tile_shapes)
+        st.tile_shape = ctypes.cast(self._shape_arr, ctypes.POINTER(ctypes.c_int32))
+        st.dtype = VSA_BF16 if self.dtype == "bf16" else VSA_F32
+        self._struct = st
+
+    @property
+    def ref(self):
+        return ctypes.byref(self._struct)
+
+
+def vsa_query_sizes(prob: Problem, sparsity: float) -> vsa_sizes:
+    sz = vsa_sizes()
+    _check("vsa_query_sizes", lib().vsa_query_sizes(prob.ref, float(sparsity), ctypes.byref(sz)))
+    return sz
+
+
+def vsa_pooled_bytes(prob: Problem, mode: int, proj_dim: int) -> int:
+    b = ctypes.c_int64()
+    _check("vsa_pooled_bytes", lib().vsa_pooled_bytes(prob.ref, int(mode), int(proj_dim),
+                                                      ctypes.byref(b)))
+    return b.value
+
+
+def vsa_kept_stats(prob: Problem, sparsity: float):
+    kept, frac = ctypes.c_int64(), ctypes.c_double()
+    _check("vsa_kept_stats", lib().vsa_kept_stats(prob.ref, float(sparsity),
+                                                  ctypes.byref(kept), ctypes.byref(frac)))
+    return kept.value, frac.value
+
+
+def vsa_count_flops(prob: Problem, sparsity: float, slot_to_token_host, kv_idx_host=None):
+    """Effective FLOPs; the arrays are host int32 numpy arrays."""
+    import numpy as np
+    s2t = np.ascontiguousarray(slot_to_token_host, dtype=np.int32)
+    kvp = None
+    if kv_idx_host is not None:
+        kv = np.ascontiguousarray(kv_idx_host, dtype=np.int32)
+        kvp = kv.ctypes.data
+    out = ctypes.c_double()
+    _check("vsa_count_flops", lib().vsa_count_flops(prob.ref, float(sparsity), s2t.ctypes.data,
+                                                    kvp, ctypes.byref(out)))
+    return out.value
+
+
+# ---------------------------------------------------------------- device calls
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _elem_dtype(prob: Problem):
+    import torch
+    return torch.bfloat16 if prob.dtype == "bf16" else torch.float32
+
+
+def _need(t, numel, dtype, name):
+    if t is None:
+        return
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    if t.dtype != dtype or t.numel() < numel:
+        raise ValueError(f"{name}: need {numel} elements of {dtype}, got "
+                         f"{t.numel()} of {t.dtype}")
+
+
+def vsa_map_tiles(prob: Problem, q, k, v, slot_to_token, qt, kt, vt, stream=None):
+    sz = vsa_query_sizes(prob, 0.0)
+    import torch
+    et = _elem_dtype(prob)
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _need(x, prob.B * prob.H * prob.N * prob.d, et, name)
+    for name, x in (("qt", qt), ("kt", kt), ("vt", vt)):
+        _need(x, sz.tiled_elems, et, name)
+    _need(slot_to_token, sz.map_elems, torch.int32, "slot_to_token")
+    _check("vsa_map_tiles", lib().vsa_map_tiles(
+        prob.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(slot_to_token), _ptr(qt), _ptr(kt),
+        _ptr(vt), _stream(stream)))
+
+
+def vsa_tile_scores(prob: Problem, mode: int, proj_dim: int, qt, kt, slot_to_token, wq, wk,
+                    pooled_ws, scores, stream=None):
+    import torch
+    sz = vsa_query_sizes(prob, 0.0)
+    _need(scores, sz.score_elems, torch.float32, "scores")
+    _need(wq, 1, torch.float32, "wq")
+    _need(wk, 1, torch.float32, "wk")
+    if pooled_ws.numel() * pooled_ws.element_size() < vsa_pooled_bytes(prob, mode, proj_dim):
+        raise ValueError("pooled_ws too small")
+    _check("vsa_tile_scores", lib().vsa_tile_scores(
+        prob.ref, int(mode), int(proj_dim), _ptr(qt), _ptr(kt), _ptr(slot_to_token), _ptr(wq),
+        _ptr(wk), _ptr(pooled_ws), _ptr(scores), _stream(stream)))
+
+
+def vsa_select_topk(prob: Problem, scores, sparsity: float, kv_idx, stream=None):
+    import torch
+    sz = vsa_query_sizes(prob, sparsity)
+    _need(scores, sz.score_elems, torch.float32, "scores")
+    _need(kv_idx, sz.idx_elems, torch.int32, "kv_idx")
+    _check("vsa_select_topk", lib().vsa_select_topk(
+        prob.ref, _ptr(scores), float(sparsity), _ptr(kv_idx), _stream(stream)))
+
+
+def vsa_sparse_attn_fwd(prob: Problem, qt, kt, vt, slot_to_token, kv_idx, sparsity: float,
+                        softmax_scale: float, out, lse=None, stream=None):
+    import torch
+    sz = vsa_query_sizes(prob, sparsity)
+    et = _elem_dtype(prob)
+    for name, x in (("qt", qt), ("kt", kt), ("vt", vt)):
+        _need(x, sz.tiled_elems, et, name)
+    _need(out, sz.out_elems, et, "out")
+    _need(lse, prob.B * prob.H * prob.N, torch.float32, "lse")
+    if kv_idx is not None:
+        _need(kv_idx, sz.idx_elems, torch.int32, "kv_idx")
+    _check("vsa_sparse_attn_fwd", lib().vsa_sparse_attn_fwd(
+        prob.ref, _ptr(qt), _ptr(kt), _ptr(vt), _ptr(slot_to_token), _ptr(kv_idx),
+        float(sparsity), float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+# ---------------------------------------------------------- whole-layer helper
+
+class Layer:
+    """Device buffers for one layer and the four calls in order.
+
+    Allocates with torch on the current device: slot_to_token, tiled Q/K/V,
+    the pooling workspace, scores, kv_idx, out and lse.
+    """
+
+    def __init__(self, prob: Problem, sparsity: float, mode: int, proj_dim: int,
+                 device="cuda", with_lse: bool = True):
+        import torch
+        self.prob, self.sparsity, self.mode, self.proj_dim = prob, sparsity, mode, proj_dim
+        self.sizes = sz = vsa_query_sizes(prob, sparsity)
+        et = _elem_dtype(prob)
+        dev = torch.device(device)
+        self.slot_to_token = torch.empty(sz.map_elems, dtype=torch.int32, device=dev)
+        self.qt, self.kt, self.vt = (torch.empty(sz.tiled_elems, dtype=et, device=dev)
+                                     for _ in range(3))
+        nbytes = vsa_pooled_bytes(prob, mode, proj_dim)
+        self.pooled = torch.empty((nbytes + 7) // 8, dtype=torch.float64, device=dev)
+        self.scores = torch.empty(sz.score_elems, dtype=torch.float32, device=dev)
+        self.kv_idx = torch.empty(max(1, sz.idx_elems), dtype=torch.int32, device=dev)
+        self.out = torch.empty((prob.B, prob.H, prob.N, prob.d), dtype=et, device=dev)
+        self.lse = (torch.empty((prob.B, prob.H, prob.N), dtype=torch.float32, device=dev)
+                    if with_lse else None)
+
+    def map_tiles(self, q, k, v, stream=None):
+        vsa_map_tiles(self.prob, q, k, v, self.slot_to_token, self.qt, self.kt, self.vt, stream)
+
+    def tile_scores(self, wq, wk, stream=None):
+        vsa_tile_scores(self.prob, self.mode, self.proj_dim, self.qt, self.kt,
+                        self.slot_to_token, wq, wk, self.pooled, self.scores, stream)
+
+    def select(self, stream=None):
+        vsa_select_topk(self.prob, self.scores, self.sparsity, self.kv_idx, stream)
+
+    def attend(self, softmax_scale: float = 0.0, stream=None, kv_idx=None):
+        kv = self.kv_idx if kv_idx is None else kv_idx
+        vsa_sparse_attn_fwd(self.prob, self.qt, self.kt, self.vt, self.slot_to_token,
+                            None if self.sparsity == 0.0 else kv, self.sparsity,
+                            softmax_scale, self.out, self.lse, stream)
+
+    def forward(self, q, k, v, wq, wk, softmax_scale: float = 0.0, stream=None):
+        """One whole layer: map+gather, scores, top-k, attention."""
+        self.map_tiles(q, k, v, stream)
+        if self.sparsity != 0.0:
+            self.tile_scores(wq, wk, stream)
+            self.select(stream)
+        self.attend(softmax_scale, stream)
+        return self.out
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)

@@ -1,0 +1,257 @@
+/*
+ * vsa.h - tile-sparse video attention on AMD Instinct MI355X (gfx950).
+ *
+ * The method (one attention layer of a video diffusion transformer):
+ *   1. tile map      prefix segments (text, reference image, reference audio)
+ *                    go into segment-pure 64-token tiles; video tokens go
+ *                    into 3D tiles of (pt, ph, pw), pt*ph*pw = 64.
+ *   2. tile scores   each (video query tile, video key tile) pair gets a
+ *                    coarse score from pooled Q/K tiles.
+ *   3. top-k         each video query tile keeps its k best video key tiles.
+ *   4. attention     flash-style softmax attention that visits only the
+ *                    prefix tiles and the kept video tiles; prefix query rows
+ *                    attend to everything.
+ * Sources: "Ref2VA VSA: нода разреженного внимания для H3 reference-to-video"
+ * (section "Патч внимания с двумя уровнями"); "Veda Sparse Attention в
+ * ComfyUI: ускорение MiniMax H3" (section "Что делает Veda");
+ * "BSAI-ComfyUI-VedaSparse" README (Overview table; Implementation);
+ * "From 650 s to 72 s: reference-to-video on a single RTX 4090" (section
+ * "The method").
+ *
+ * Conventions for every entry point
+ *   - Host-callable, thread-safe, no global state.
+ *   - Device pointers are owned by the caller. The library never allocates,
+ *     frees or keeps a pointer after it returns.
+ *   - `stream` is a hipStream_t (NULL = the default stream). All device work
+ *     is enqueued on it; no entry point synchronises.
+ *   - Return VSA_OK (0) or a negative vsa_status. Every argument error is
+ *     found on the host before anything is launched; nothing falls back to a
+ *     slower path silently (the caller decides about a dense fallback).
+ *     VSA_ERR_HIP reports a failed launch; faults inside a kernel surface at
+ *     the caller's next synchronisation.
+ *
+ * Sequence layout: Q, K, V and O are [B][H][N][d], d contiguous, with
+ * N = sum(prefix_len) + T*Hv*Wv: the prefix segments in caller order, then
+ * video tokens row-major in (t, y, x).
+ */
+#ifndef VSA_H
+#define VSA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VSA_API __attribute__((visibility("default")))
+
+#define VSA_VERSION 100             /* 1.0.0 */
+#define VSA_TILE 64                 /* tokens per tile */
+#define VSA_MAX_SEGMENTS 8          /* prefix segments */
+#define VSA_MAX_SHAPES 16           /* distinct per-head tile shapes */
+#define VSA_MAX_VIDEO_TILES 8192    /* video tiles per head (top-k row length) */
+#define VSA_MAX_PROJ 64             /* TripPool projection width */
+
+typedef enum vsa_status {
+  VSA_OK = 0,
+  VSA_ERR_INVALID_ARG = -1,   /* null pointer, bad geometry, N mismatch,
+                                 tile product != 64, sparsity out of range */
+  VSA_ERR_UNSUPPORTED = -2,   /* d or dtype the kernels do not implement */
+  VSA_ERR_SIZE = -3,          /* a count exceeds a documented limit */
+  VSA_ERR_HIP = -4            /* a HIP call or kernel launch failed */
+} vsa_status;
+
+typedef enum vsa_dtype { VSA_F32 = 0, VSA_BF16 = 1 } vsa_dtype;
+
+typedef enum vsa_score_mode {
+  VSA_SCORE_MEAN_GATE = 0,    /* VSA: mean-pool, then the per-head gate */
+  VSA_SCORE_TRIPPOOL = 1      /* Veda: project tokens, then Avg|Max|Min */
+} vsa_score_mode;
+
+/* One attention layer's geometry. */
+typedef struct vsa_problem {
+  int32_t B, H, N, d;         /* batch, heads, tokens, head dim (64 or 128) */
+  int32_t T, Hv, Wv;          /* latent video grid */
+  int32_t n_prefix;           /* 0..VSA_MAX_SEGMENTS prefix segments */
+  int32_t prefix_len[VSA_MAX_SEGMENTS];  /* lengths in sequence order; each
+                                 segment fills its own ceil(len/64) tiles,
+                                 a zero length gives no tile */
+  int32_t n_shapes;           /* 1..VSA_MAX_SHAPES */
+  const int32_t *tile_shape;  /* HOST pointer, [n_shapes][3] = (pt, ph, pw),
+                                 pt*ph*pw == 64; head h uses shape
+                                 h % n_shapes; each grid axis is padded up to a
+                                 multiple of the tile edge */
+  int32_t dtype;              /* vsa_dtype of Q, K, V, the tiled copies and O */
+} vsa_problem;
+
+/* Buffer sizes and per-shape counts, from vsa_query_sizes. */
+typedef struct vsa_sizes {
+  int64_t map_elems;          /* int32 elements of slot_to_token */
+  int64_t tiled_elems;        /* dtype elements of each of qt, kt, vt */
+  int64_t pooled_rows;        /* rows of the pooling workspace (see
+                                 vsa_pooled_bytes) */
+  int64_t score_elems;        /* float elements of scores */
+  int64_t idx_elems;          /* int32 elements of kv_idx */
+  int64_t out_elems;          /* dtype elements of out: B*H*N*d */
+  int32_t n_prefix_tiles;     /* same for every shape */
+  int32_t max_tiles;          /* max over shapes of n_tiles */
+  int32_t max_video_tiles;    /* max over shapes of n_video_tiles */
+  int32_t k_max;              /* max over shapes of k */
+  int32_t keep_bp;            /* kept share of video key tiles, basis points */
+  int32_t n_tiles[VSA_MAX_SHAPES];        /* prefix + video tiles */
+  int32_t n_video_tiles[VSA_MAX_SHAPES];
+  int32_t k[VSA_MAX_SHAPES];  /* video key tiles kept per video query tile */
+} vsa_sizes;
+
+/*
+ * vsa_query_sizes - validate a problem and report buffer sizes. Host only,
+ * makes no HIP call.
+ *
+ * sparsity in [0, 1) is turned into keep_bp = round((1 - sparsity) * 10^4)
+ * once; per shape k = max(1, ceil(keep_bp * n_video_tiles / 10^4)) in
+ * integer arithmetic ("75% sparsity" keeps the top 25% of video key tiles:
+ * "From 650 s to 72 s", section "Where the time went"). sparsity == 0 is
+ * the dense path (k = n_video_tiles).
+ */
+VSA_API int vsa_query_sizes(const vsa_problem *prob, double sparsity,
+                            vsa_sizes *sizes);
+
+/*
+ * vsa_pooled_bytes - bytes of the pooling workspace of vsa_tile_scores:
+ * pooled_rows * r * 8, r = d (mean gate) or 3 * proj_dim (TripPool).
+ */
+VSA_API int vsa_pooled_bytes(const vsa_problem *prob, int32_t mode,
+                             int32_t proj_dim, int64_t *bytes);
+
+/*
+ * Tiled layouts (per tile: 64 slots x d channels, dtype elements).
+ *
+ * qt, kt ("row operand" layout): element (slot s, channel c) at
+ *   ((s/32)*(d/16) + c/16)*512 + (((c%16)/8)*32 + s%32)*8 + c%8
+ * vt ("column operand" layout): element (s, c) at
+ *   ((c/32)*4 + s/16)*512 + (((s%8)/4)*32 + c%32)*8 + ((s%16)/8)*4 + s%4
+ * Both are permutations of the tile's 64*d elements; pad slots hold zero.
+ * Tile t of head (b, h) starts at element ((b*H + h)*max_tiles + t)*64*d.
+ * Tiles beyond the head's own n_tiles are not written.
+ *
+ * slot_to_token: int32 [n_shapes][max_tiles][64]; the token index held by a
+ * slot, -1 for a pad. Prefix segment s (offset o_s, length L_s) fills
+ * ceil(L_s/64) tiles, slot j -> o_s + j while j < L_s. Video tile
+ * (ti, hi, wi) is tile n_prefix_tiles + (ti*nh + hi)*nw + wi, slot
+ * (a*ph + b)*pw + c -> token P + (t*Hv + y)*Wv + x with
+ * (t, y, x) = (ti*pt + a, hi*ph + b, wi*pw + c), or -1 outside the grid.
+ * Entries of tiles beyond a shape's n_tiles are -1.
+ */
+
+/*
+ * vsa_map_tiles - step 1: build slot_to_token and gather Q, K, V into the
+ * tiled layouts (segment-pure prefix tiles: "Ref2VA VSA" node news, section
+ * "Патч внимания с двумя уровнями", item 1; whole-tile row gather:
+ * "BSAI-ComfyUI-VedaSparse" README, Implementation section).
+ *
+ * q, k, v: [B][H][N][d] dtype, device. Any of the three may be NULL together
+ * with its tiled output (that tensor is skipped). slot_to_token (device,
+ * map_elems) is always written. qt, kt, vt: device, tiled_elems each.
+ */
+VSA_API int vsa_map_tiles(const vsa_problem *prob, const void *q,
+                          const void *k, const void *v, int32_t *slot_to_token,
+                          void *qt, void *kt, void *vt, void *stream);
+
+/*
+ * vsa_tile_scores - step 2: pooled tile descriptors and their dot products.
+ *
+ * mode VSA_SCORE_MEAN_GATE (VSA): desc = mean of a video tile's real rows
+ *   times the head's gate (to_gate_compress: "From 650 s to 72 s", section
+ *   "The method"). wq: float [H][d][d] gate applied to pooled Q; wk: gate for
+ *   pooled K, or NULL to use wq for both. proj_dim must equal d.
+ * mode VSA_SCORE_TRIPPOOL (Veda): each real token of a video tile is
+ *   projected by the head's d x proj_dim matrix, then [Avg | Max | Min] over
+ *   the tile's real tokens (TripPool: "BSAI-ComfyUI-VedaSparse" README,
+ *   Overview table). wq, wk: float [H][d][proj_dim]; proj_dim a power of two
+ *   in 8..VSA_MAX_PROJ.
+ * Pads never enter a descriptor. Descriptors are accumulated in double.
+ *
+ * scores: float [B][H][max_video_tiles][max_video_tiles], row = video query
+ *   tile i, column = video key tile j (video-local indices), the double dot
+ *   product of the two descriptors rounded once to float. Only the head's
+ *   n_video_tiles x n_video_tiles block is written. Prefix tiles are never
+ *   scored.
+ * pooled_ws: device workspace of vsa_pooled_bytes bytes (holds the double
+ *   descriptors, Q rows first, then K rows).
+ * qt, kt, slot_to_token: as written by vsa_map_tiles.
+ */
+VSA_API int vsa_tile_scores(const vsa_problem *prob, int32_t mode,
+                            int32_t proj_dim, const void *qt, const void *kt,
+                            const int32_t *slot_to_token, const float *wq,
+                            const float *wk, void *pooled_ws, float *scores,
+                            void *stream);
+
+/*
+ * vsa_select_topk - step 3: per (b, h, video query tile i), keep the k best
+ * video key tiles: higher score first, lower tile index first among equal
+ * scores (-0.0 equals +0.0); tile j is kept iff
+ * #{j' : s_j' > s_j} + #{j' < j : s_j' = s_j} < k. Top-k pruning applies to
+ * video key tiles only ("Ref2VA VSA" node news, item 2).
+ *
+ * kv_idx: int32 [B][H][max_video_tiles][k_max]; row i holds the k kept
+ * video-local tile indices in ascending order, then -1 up to k_max.
+ * Scores must be finite.
+ */
+VSA_API int vsa_select_topk(const vsa_problem *prob, const float *scores,
+                            double sparsity, int32_t *kv_idx, void *stream);
+
+/*
+ * vsa_sparse_attn_fwd - step 4: for every real query token t,
+ *   O_t = softmax_u(q_t . k_u * scale) V_u over its allowed real keys u.
+ * A video query tile is allowed every prefix tile and its kv_idx video
+ * tiles (tile skipping: "Veda Sparse Attention в ComfyUI", section "Что
+ * делает Veda"); a prefix query tile is allowed every tile (conditioning rows
+ * stay exact: "BSAI-ComfyUI-VedaSparse" README, v3.4 highlights). Pad slots
+ * are neither queries nor keys.
+ *
+ * qt, kt, vt, slot_to_token: from vsa_map_tiles. kv_idx: from
+ * vsa_select_topk with the same sparsity; may be NULL when sparsity == 0
+ * (dense: every tile allowed). softmax_scale <= 0 selects 1/sqrt(d).
+ * out: [B][H][N][d] dtype, each token's row written at its own position.
+ * lse: float [B][H][N] natural-log sum of exp of the scaled logits, or NULL.
+ * VSA_BF16: bf16 inputs, fp32 accumulation and softmax, bf16 output.
+ * VSA_F32: fp32 throughout.
+ */
+VSA_API int vsa_sparse_attn_fwd(const vsa_problem *prob, const void *qt,
+                                const void *kt, const void *vt,
+                                const int32_t *slot_to_token,
+                                const int32_t *kv_idx, double sparsity,
+                                float softmax_scale, void *out, float *lse,
+                                void *stream);
+
+/*
+ * vsa_kept_stats - host only: tile pairs the attention visits and their
+ * share of full attention's tile pairs (the "attention computed: x% of full
+ * attention" report of "Veda Sparse Attention в ComfyUI", section "Узел
+ * ComfyUI").
+ */
+VSA_API int vsa_kept_stats(const vsa_problem *prob, double sparsity,
+                           int64_t *kept_tile_pairs, double *frac_of_full);
+
+/*
+ * vsa_count_flops - host only: effective FLOPs of vsa_sparse_attn_fwd,
+ * 4*d * sum over real query tokens of their allowed real keys (QK^T and PV,
+ * two flops per multiply-add; softmax not counted).
+ * slot_to_token_host, kv_idx_host: HOST copies of the device arrays
+ * (kv_idx_host may be NULL when sparsity == 0).
+ */
+VSA_API int vsa_count_flops(const vsa_problem *prob, double sparsity,
+                            const int32_t *slot_to_token_host,
+                            const int32_t *kv_idx_host, double *flops);
+
+/* Static text for a vsa_status value. */
+VSA_API const char *vsa_status_string(int status);
+
+/* VSA_VERSION of the built library. */
+VSA_API int vsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VSA_H */

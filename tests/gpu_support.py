@@ -1,0 +1,198 @@
+"""Helpers for the GPU parity tests: run the library, run the oracle on the
+same seeded inputs, unpack the tiled layouts, and compare.
+
+The tiled-layout formulas below are restated from include/vsa.h (the ABI
+contract); they are test-side readers of the library's output, not shared
+code. Nothing here computes any step of the method: the expected values come
+from the oracle alone.
+"""
+from __future__ import annotations
+
+import math
+import sys
+from dataclasses import dataclass
+
+import numpy as np
+
+import oracle
+from workloads import Workload
+from workloads.inputs import bf16_to_f32, make_qkv, make_weights
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# ------------------------------------------------------------ tiled layouts
+
+def row_layout_index(d: int) -> np.ndarray:
+    """perm[s*d + c] = offset of (slot s, channel c) in a Q/K tile."""
+    s = np.arange(64)[:, None]
+    c = np.arange(d)[None, :]
+    off = ((s // 32) * (d // 16) + c // 16) * 512 + (((c % 16) // 8) * 32 + s % 32) * 8 + c % 8
+    return off.reshape(-1)
+
+
+def col_layout_index(d: int) -> np.ndarray:
+    """perm[s*d + c] = offset of (slot s, channel c) in a V tile."""
+    s = np.arange(64)[:, None]
+    c = np.arange(d)[None, :]
+    off = ((c // 32) * 4 + s // 16) * 512 + (((s % 8) // 4) * 32 + c % 32) * 8 \
+        + ((s % 16) // 8) * 4 + s % 4
+    return off.reshape(-1)
+
+
+def unpack_tiles(flat: np.ndarray, n_tiles: int, d: int, col: bool) -> np.ndarray:
+    """[n_tiles*64*d] tiled layout -> [n_tiles, 64, d] plain rows."""
+    perm = col_layout_index(d) if col else row_layout_index(d)
+    t = flat[: n_tiles * 64 * d].reshape(n_tiles, 64 * d)
+    return t[:, perm].reshape(n_tiles, 64, d)
+
+
+# ------------------------------------------------------------ library runs
+
+@dataclass
+class GpuRun:
+    w: Workload
+    prob: object
+    layer: object
+    q: object
+    k: object
+    v: object
+    wq: object
+    wk: object
+
+
+def to_device(w: Workload, heads=None, arrays=None):
+    """Q, K, V on the device; ``arrays`` (float32 [B, H, N, d], bf16-exact for
+    bf16 workloads) overrides the seeded generator."""
+    import torch
+    from workloads.inputs import bf16_bits
+    if arrays is None:
+        q, k, v = make_qkv(w, heads=heads, as_bf16_bits=(w.dtype == "bf16"))
+    elif w.dtype == "bf16":
+        q, k, v = (bf16_bits(np.ascontiguousarray(a, dtype=np.float32)) for a in arrays)
+    else:
+        q, k, v = (np.ascontiguousarray(a, dtype=np.float32) for a in arrays)
+    if w.dtype == "bf16":
+        t = [torch.from_numpy(x).view(torch.bfloat16).cuda() for x in (q, k, v)]
+    else:
+        t = [torch.from_numpy(x).cuda() for x in (q, k, v)]
+    return t
+
+
+def problem_of(w: Workload, H=None):
+    from block_sparse_video_map_amd import vsa
+    return vsa.Problem(w.B, w.H if H is None else H, w.d, w.grid, w.prefix, w.tile_shapes,
+                       w.dtype)
+
+
+def run_library(w: Workload, sparsity=None, stages=("map", "score", "select", "attn"),
+                arrays=None):
+    """Runs the library's layer on the workload's seeded inputs (all heads)."""
+    import torch
+    from block_sparse_video_map_amd import vsa
+    sp = w.sparsity if sparsity is None else sparsity
+    prob = problem_of(w)
+    mode = vsa.VSA_SCORE_MEAN_GATE if w.scorer == "mean_gate" else vsa.VSA_SCORE_TRIPPOOL
+    proj = w.d if w.scorer == "mean_gate" else w.proj_dim
+    layer = vsa.Layer(prob, sp, mode, proj)
+    q, k, v = to_device(w, arrays=arrays)
+    W = make_weights(w)
+    if w.scorer == "mean_gate":
+        wq = torch.from_numpy(W["gate"]).cuda()
+        wk = None
+    else:
+        wq = torch.from_numpy(W["proj_q"]).cuda()
+        wk = torch.from_numpy(W["proj_k"]).cuda()
+    layer.map_tiles(q, k, v)
+    if "score" in stages and sp != 0.0:
+        layer.tile_scores(wq, wk)
+    if "select" in stages and sp != 0.0:
+        layer.select()
+    if "attn" in stages:
+        layer.attend()
+    torch.cuda.synchronize()
+    return GpuRun(w, prob, layer, q, k, v, wq, wk)
+
+
+def tensor_f32(t) -> np.ndarray:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return bf16_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16))
+    return t.cpu().numpy()
+
+
+# ------------------------------------------------------------ oracle runs
+
+def head_inputs(w: Workload, h: int, b: int = 0):
+    from workloads.inputs import head_qkv
+    return head_qkv(w, b, h)
+
+
+def oracle_head(w: Workload, h: int, sparsity=None, query_tiles=(), b: int = 0,
+                arrays=None):
+    """The oracle's whole path for one head (attention only on query_tiles)."""
+    if arrays is None:
+        q, k, v = head_inputs(w, h, b)
+    else:
+        q, k, v = (np.asarray(a[b, h], dtype=np.float32) for a in arrays)
+    W = make_weights(w)
+    shape = w.tile_shapes[h % len(w.tile_shapes)]
+    if w.scorer == "mean_gate":
+        wq, wk = W["gate"][h], None
+    else:
+        wq, wk = W["proj_q"][h], W["proj_k"][h]
+    sp = w.sparsity if sparsity is None else sparsity
+    qt = None if query_tiles is None else list(query_tiles)
+    return oracle.head_forward(q, k, v, w.grid, w.prefix, shape, sp, w.scorer, wq, wk,
+                               query_tiles=qt), (q, k, v)
+
+
+# ------------------------------------------------------------ comparisons
+
+def band_rule_check(scores_orc: np.ndarray, sel_gpu: np.ndarray, k: int, rel=1e-6):
+    """Selection comparison with near-ties excluded.
+
+    Returns (n_rows_differing, n_rows_with_band_gt1, failures).
+    For each row: tau = k-th ranked oracle score; A = near-ties of tau. The
+    GPU list must be k strictly ascending entries, contain every j outside A
+    scoring above tau and no j outside A scoring below tau.
+    """
+    n_q, n = scores_orc.shape
+    sel_orc = oracle.select_topk(scores_orc, k)
+    differ, wide, fails = 0, 0, []
+    for i in range(n_q):
+        g = sel_gpu[i, :k]
+        if not (np.all(np.diff(g) > 0) and g.min() >= 0 and g.max() < n):
+            fails.append((i, "not strictly ascending / out of range"))
+            continue
+        if np.array_equal(g, sel_orc[i]):
+            continue
+        differ += 1
+        s = scores_orc[i].astype(np.float64)
+        order = np.lexsort((np.arange(n), -scores_orc[i]))
+        tau = s[order[k - 1]]
+        band = np.abs(s - tau) <= rel * np.maximum(np.abs(s), abs(tau))
+        if band.sum() > 1:
+            wide += 1
+        gs = set(g.tolist())
+        must = set(np.nonzero((s > tau) & ~band)[0].tolist())
+        never = set(np.nonzero((s < tau) & ~band)[0].tolist())
+        if not must <= gs or gs & never:
+            fails.append((i, "outside the near-tie band"))
+    return differ, wide, fails
+
+
+def bf16_stats(got: np.ndarray, want: np.ndarray):
+    diff = np.abs(got.astype(np.float64) - want)
+    return float(diff.max()), float(diff.mean())
+
+
+BF16_MAX_ABS, BF16_MEAN_ABS = 2e-2, 5e-3
+F32_MAX_ABS = 1e-5
+
+
+def default_scale(d):
+    return 1.0 / math.sqrt(d)

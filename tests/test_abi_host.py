@@ -1,0 +1,195 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol,
+plans sizes correctly and rejects bad arguments before any launch (CPU only;
+no compute call is made)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from block_sparse_video_map_amd import vsa
+from workloads import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vsa.h")
+
+
+def _problem(w, **kw):
+    args = dict(B=w.B, H=w.H, d=w.d, grid=w.grid, prefix=w.prefix,
+                tile_shapes=w.tile_shapes, dtype=w.dtype)
+    args.update(kw)
+    return vsa.Problem(**args)
+
+
+def test_every_declared_symbol_is_exported():
+    decl = re.findall(r"VSA_API\s+[^;(]*?\b(vsa_\w+)\s*\(", open(HEADER).read())
+    assert set(decl) == set(vsa.EXPORTS)
+    L = vsa.lib()
+    for name in decl:
+        assert hasattr(L, name), name
+    assert vsa.vsa_version() == 100
+
+
+def test_struct_layout_matches_header(tmp_path):
+    """ctypes mirrors of the structs agree with the C compiler's layout."""
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "vsa.h"\n'
+        'int main(void){printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(vsa_problem),'
+        ' offsetof(vsa_problem, tile_shape), offsetof(vsa_problem, dtype),'
+        ' sizeof(vsa_sizes), offsetof(vsa_sizes, keep_bp), offsetof(vsa_sizes, k));'
+        ' return 0;}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    want = [ctypes.sizeof(vsa.vsa_problem), vsa.vsa_problem.tile_shape.offset,
+            vsa.vsa_problem.dtype.offset, ctypes.sizeof(vsa.vsa_sizes),
+            vsa.vsa_sizes.keep_bp.offset, vsa.vsa_sizes.k.offset]
+    assert got == want
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_sizes_agree_with_oracle_counts(name):
+    w = WORKLOADS[name]
+    sz = vsa.vsa_query_sizes(_problem(w), w.sparsity)
+    tms = [oracle.tile_map(*w.grid, w.prefix, s) for s in w.tile_shapes]
+    assert sz.n_prefix_tiles == tms[0].n_prefix_tiles
+    for i, tm in enumerate(tms):
+        assert sz.n_tiles[i] == tm.n_tiles
+        assert sz.n_video_tiles[i] == tm.n_video_tiles
+        assert sz.k[i] == oracle.keep_count(w.sparsity, tm.n_video_tiles)
+    assert sz.max_tiles == max(t.n_tiles for t in tms)
+    assert sz.tiled_elems == w.B * w.H * sz.max_tiles * 64 * w.d
+    assert sz.out_elems == w.B * w.H * w.N * w.d
+
+
+def test_headline_counts():
+    w = WORKLOADS["3a"]
+    sz = vsa.vsa_query_sizes(_problem(w), 0.75)
+    assert (sz.n_prefix_tiles, sz.n_video_tiles[0], sz.k[0]) == (3, 1764, 441)
+    kept, frac = vsa.vsa_kept_stats(_problem(w), 0.75)
+    assert kept == 24 * (3 * 1767 + 1764 * (3 + 441))
+    assert abs(frac - (3 * 1767 + 1764 * 444) / 1767 ** 2) < 1e-12
+    kept0, frac0 = vsa.vsa_kept_stats(_problem(w), 0.0)
+    assert frac0 == 1.0
+
+
+def test_keep_counts_match_oracle_over_a_sweep():
+    for sp in np.linspace(0, 0.999, 97):
+        for n in (1, 3, 4, 17, 504, 1764, 3780, 4032):
+            p = vsa.Problem(1, 1, 64, (1, 1, n), (), ((1, 1, 64),), "bf16") if n <= 8192 else None
+            sz = vsa.vsa_query_sizes(p, float(sp))
+            tiles = (n + 63) // 64
+            assert sz.k[0] == oracle.keep_count(float(sp), tiles)
+
+
+def test_count_flops_matches_oracle_on_host_arrays():
+    w = WORKLOADS["1"]
+    p = _problem(w)
+    tm = oracle.tile_map(*w.grid, w.prefix, w.tile_shapes[0])
+    rng = np.random.default_rng(0)
+    sz = vsa.vsa_query_sizes(p, 0.5)
+    kv = np.full((w.B * w.H, sz.max_video_tiles, sz.k_max), -1, dtype=np.int32)
+    sels = []
+    for h in range(w.H):
+        sel = np.sort(np.stack([rng.choice(tm.n_video_tiles, sz.k[0], replace=False)
+                                for _ in range(tm.n_video_tiles)]), axis=1)
+        kv[h, :, :sz.k[0]] = sel
+        sels.append(sel)
+    s2t = tm.slot_to_token.astype(np.int32)
+    got = vsa.vsa_count_flops(p, 0.5, s2t, kv)
+    want = sum(oracle.effective_flops(tm, oracle.allowed_tiles(tm, s), w.d) for s in sels)
+    assert got == want
+    dense = vsa.vsa_count_flops(p, 0.0, s2t, None)
+    assert dense == w.H * 4 * w.d * w.N * w.N
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(d=96), vsa.VSA_ERR_UNSUPPORTED),
+    (dict(dtype="f16"), None),
+    (dict(tile_shapes=((4, 4, 5),)), vsa.VSA_ERR_INVALID_ARG),
+    (dict(tile_shapes=((0, 8, 8),)), vsa.VSA_ERR_INVALID_ARG),
+    (dict(N=999), vsa.VSA_ERR_INVALID_ARG),
+    (dict(grid=(0, 8, 8)), vsa.VSA_ERR_INVALID_ARG),
+    (dict(prefix=(-1,)), vsa.VSA_ERR_INVALID_ARG),
+    (dict(grid=(1, 1, 64 * 8193), prefix=(), tile_shapes=((1, 1, 64),)), vsa.VSA_ERR_SIZE),
+])
+def test_invalid_problems_rejected(change, status):
+    w = WORKLOADS["1"]
+    p = _problem(w, **change)
+    if status is None:            # unknown dtype string maps to f32 here: still valid
+        vsa.vsa_query_sizes(p, 0.75)
+        return
+    with pytest.raises(vsa.VSAError) as e:
+        vsa.vsa_query_sizes(p, 0.75)
+    assert e.value.status == status
+
+
+@pytest.mark.parametrize("sp", [-0.1, 1.0, 1.5, math.nan, math.inf])
+def test_sparsity_out_of_range(sp):
+    with pytest.raises(vsa.VSAError) as e:
+        vsa.vsa_query_sizes(_problem(WORKLOADS["1"]), sp)
+    assert e.value.status == vsa.VSA_ERR_INVALID_ARG
+
+
+def test_null_arguments_rejected_before_launch():
+    """Every device entry point returns an error on null/misaligned buffers
+    without touching the GPU (these calls never reach a launch). Runs only
+    where no GPU is visible, so that a validation bug can never turn the fake
+    pointers below into a real launch."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host-only check; skipped where a GPU is visible")
+    L = vsa.lib()
+    p = _problem(WORKLOADS["1"])
+    fake = ctypes.c_void_p(0x10000)          # never dereferenced: rejected first
+    odd = ctypes.c_void_p(0x10008)
+    assert L.vsa_map_tiles(None, fake, fake, fake, fake, fake, fake, fake, None) \
+        == vsa.VSA_ERR_INVALID_ARG
+    assert L.vsa_map_tiles(p.ref, fake, fake, fake, None, fake, fake, fake, None) \
+        == vsa.VSA_ERR_INVALID_ARG
+    assert L.vsa_map_tiles(p.ref, fake, None, fake, fake, fake, fake, fake, None) \
+        == vsa.VSA_ERR_INVALID_ARG
+    assert L.vsa_map_tiles(p.ref, odd, fake, fake, fake, fake, fake, fake, None) \
+        == vsa.VSA_ERR_INVALID_ARG
+    assert L.vsa_tile_scores(p.ref, 0, 64, fake, fake, fake, None, None, fake, fake, None) \
+        == vsa.VSA_ERR_INVALID_ARG
+    assert L.vsa_tile_scores(p.ref, 0, 32, fake, fake, fake, fake, None, fake, fake, None) \
+        == vsa.VSA_ERR_INVALID_ARG
+    assert L.vsa_tile_scores(p.ref, 1, 24, fake, fake, fake, fake, fake, fake, fake, None) \
+        == vsa.VSA_ERR_UNSUPPORTED
+    assert L.vsa_tile_scores(p.ref, 1, 32, fake, fake, fake, fake, None, fake, fake, None) \
+        == vsa.VSA_ERR_INVALID_ARG
+    assert L.vsa_tile_scores(p.ref, 7, 64, fake, fake, fake, fake, None, fake, fake, None) \
+        == vsa.VSA_ERR_INVALID_ARG
+    assert L.vsa_select_topk(p.ref, None, 0.75, fake, None) == vsa.VSA_ERR_INVALID_ARG
+    assert L.vsa_select_topk(p.ref, fake, 1.0, fake, None) == vsa.VSA_ERR_INVALID_ARG
+    assert L.vsa_sparse_attn_fwd(p.ref, fake, fake, fake, fake, None, 0.75, 0.0, fake, None,
+                                 None) == vsa.VSA_ERR_INVALID_ARG
+    assert L.vsa_sparse_attn_fwd(p.ref, fake, fake, fake, fake, fake, 0.75,
+                                 float("nan"), fake, None, None) == vsa.VSA_ERR_INVALID_ARG
+    assert L.vsa_sparse_attn_fwd(p.ref, fake, fake, odd, fake, fake, 0.75, 0.0, fake, None,
+                                 None) == vsa.VSA_ERR_INVALID_ARG
+    bad = _problem(WORKLOADS["1"], d=32)
+    assert L.vsa_sparse_attn_fwd(bad.ref, fake, fake, fake, fake, fake, 0.75, 0.0, fake, None,
+                                 None) == vsa.VSA_ERR_UNSUPPORTED
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3, -4, 5):
+        assert isinstance(vsa.status_string(st), str)
+    assert vsa.status_string(-2).startswith("unsupported")
+
+
+def test_pooled_bytes():
+    w = WORKLOADS["4a"]
+    p = _problem(w)
+    sz = vsa.vsa_query_sizes(p, 0.9)
+    assert vsa.vsa_pooled_bytes(p, 1, 32) == sz.pooled_rows * 96 * 8
+    assert vsa.vsa_pooled_bytes(p, 0, 128) == sz.pooled_rows * 128 * 8

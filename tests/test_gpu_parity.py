@@ -1,0 +1,165 @@
+"""GPU parity: every library step against the oracle on the seeded workloads.
+
+Tile maps, gathered tiles and selected indices must be bit-exact (selection
+under the near-tie band rule); scores within one float32 ulp of the oracle's
+float64 value rounded to float32; outputs within 1e-5 max-abs (fp32) or
+2e-2 max-abs and 5e-3 mean-abs (bf16). The workloads run at their full
+shape; the oracle is evaluated on sampled heads and query tiles where the
+full comparison would take it minutes.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import gpu_support as gs
+from workloads import WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+# workload -> (heads compared, attention query tiles per head: None = all)
+PLAN = {
+    "1": ([0, 1], None),
+    "2": ([0, 23], 48),
+    "4a": ([0, 1, 2], 48),
+    "3a": ([0, 12, 23], 64),
+    "3b": ([0, 23], 32),
+    "4b": ([0, 1, 2], 32),
+    "5": ([0, 1, 2], 24),
+}
+
+# VSA_PARITY_WORKLOADS="1,2" restricts the run to a subset (default: all).
+_only = os.environ.get("VSA_PARITY_WORKLOADS")
+if _only:
+    PLAN = {k: v for k, v in PLAN.items() if k in _only.split(",")}
+
+_oracle_cache = {}
+
+
+@pytest.fixture(scope="module", params=list(PLAN))
+def run(request):
+    """The library's whole layer on one workload; tests are grouped by it."""
+    import torch
+    name = request.param
+    gs.log(f"[parity] running library on workload {name}")
+    r = gs.run_library(WORKLOADS[name])
+    r.name = name
+    yield r
+    _oracle_cache.clear()
+    del r
+    torch.cuda.empty_cache()
+
+
+def _oracle(name, h, query_tiles=()):
+    key = (name, h, tuple(query_tiles))
+    if key not in _oracle_cache:
+        _oracle_cache[key] = gs.oracle_head(WORKLOADS[name], h, query_tiles=query_tiles)
+    return _oracle_cache[key]
+
+
+def _sizes(run):
+    return run.layer.sizes
+
+
+def test_tile_map_bit_exact(run):
+    name = run.name
+    w = run.w
+    sz = _sizes(run)
+    s2t = run.layer.slot_to_token.cpu().numpy().reshape(len(w.tile_shapes), sz.max_tiles * 64)
+    for si, shape in enumerate(w.tile_shapes):
+        tm = oracle.tile_map(*w.grid, w.prefix, shape)
+        want = np.full(sz.max_tiles * 64, -1, dtype=np.int64)
+        want[: tm.slot_to_token.size] = tm.slot_to_token
+        np.testing.assert_array_equal(s2t[si], want)
+
+
+def test_gather_bit_exact(run):
+    name = run.name
+    w, sz = run.w, _sizes(run)
+    per_head = sz.max_tiles * 64 * w.d
+    for h in PLAN[name][0]:
+        gs.log(f"[parity] gather {name} head {h}")
+        q, k, v = gs.head_inputs(w, h)
+        tm = oracle.tile_map(*w.grid, w.prefix, w.tile_shapes[h % len(w.tile_shapes)])
+        for x, t, col in ((q, run.layer.qt, False), (k, run.layer.kt, False),
+                          (v, run.layer.vt, True)):
+            flat = gs.tensor_f32(t[h * per_head:(h + 1) * per_head])
+            got = gs.unpack_tiles(flat, tm.n_tiles, w.d, col)
+            np.testing.assert_array_equal(got, oracle.gather(x, tm))
+
+
+def test_tile_scores_match(run):
+    name = run.name
+    w, sz = run.w, _sizes(run)
+    nv = sz.max_video_tiles
+    sc = run.layer.scores.view(w.B * w.H, nv, nv)
+    for h in PLAN[name][0]:
+        r, _ = _oracle(name, h)
+        n = r["tmap"].n_video_tiles
+        got = sc[h, :n, :n].cpu().numpy()
+        want = r["scores"]
+        ulp = np.abs(got.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
+        same = float((got == want).mean())
+        gs.log(f"[parity] scores {name} head {h}: equal {same:.6f}, max ulp {ulp.max()}")
+        assert ulp.max() <= 1
+        assert same > 0.999
+
+
+def test_select_topk_bit_exact(run):
+    name = run.name
+    w, sz = run.w, _sizes(run)
+    kv = run.layer.kv_idx[: sz.idx_elems].view(w.B * w.H, sz.max_video_tiles, sz.k_max)
+    for h in PLAN[name][0]:
+        r, _ = _oracle(name, h)
+        n, k = r["tmap"].n_video_tiles, r["k"]
+        assert k == sz.k[h % len(w.tile_shapes)]
+        got = kv[h, :n].cpu().numpy()
+        assert (got[:, k:] == -1).all()
+        differ, wide, fails = gs.band_rule_check(r["scores"], got, k)
+        gs.log(f"[parity] select {name} head {h}: k={k} rows={n} differing={differ} "
+               f"wide-band={wide}")
+        assert not fails, fails[:5]
+        assert differ <= wide
+
+
+def _pick_tiles(tm, count, seed):
+    if count is None:
+        return list(range(tm.n_tiles))
+    rng = np.random.default_rng(seed)
+    vids = rng.choice(tm.n_video_tiles, size=min(count, tm.n_video_tiles), replace=False)
+    return list(range(tm.n_prefix_tiles)) + sorted(int(tm.n_prefix_tiles + v) for v in vids)
+
+
+def test_attention_matches_oracle(run):
+    name = run.name
+    w, sz = run.w, _sizes(run)
+    heads, count = PLAN[name]
+    out = run.layer.out
+    lse = run.layer.lse
+    kv = run.layer.kv_idx[: sz.idx_elems].view(w.B * w.H, sz.max_video_tiles, sz.k_max)
+    for h in heads:
+        tm = oracle.tile_map(*w.grid, w.prefix, w.tile_shapes[h % len(w.tile_shapes)])
+        tiles = _pick_tiles(tm, count, seed=1000 + h)
+        r, _ = _oracle(name, h)
+        gpu_sel = kv[h, : tm.n_video_tiles, : r["k"]].cpu().numpy()
+        same_sel = [t for t in tiles if t < tm.n_prefix_tiles
+                    or np.array_equal(gpu_sel[t - tm.n_prefix_tiles],
+                                      r["kv_video"][t - tm.n_prefix_tiles])]
+        assert len(tiles) - len(same_sel) <= max(1, len(tiles) // 100)
+        gs.log(f"[parity] attention {name} head {h}: {len(same_sel)} query tiles")
+        ro, _ = _oracle(name, h, query_tiles=same_sel)
+        rows = np.concatenate([tm.tile_tokens(t) for t in same_sel])
+        got = gs.tensor_f32(out[0, h])[rows]
+        want = ro["out"][rows]
+        got_lse = lse[0, h].cpu().numpy()[rows]
+        mx, mean = gs.bf16_stats(got, want)
+        lse_err = float(np.abs(got_lse - ro["lse"][rows]).max())
+        gs.log(f"[parity] attention {name} head {h}: max-abs {mx:.3e} mean-abs {mean:.3e} "
+               f"lse max-abs {lse_err:.3e}")
+        if w.dtype == "f32":
+            assert mx <= gs.F32_MAX_ABS
+            assert lse_err <= gs.F32_MAX_ABS
+        else:
+            assert mx <= gs.BF16_MAX_ABS and mean <= gs.BF16_MEAN_ABS
+            assert lse_err <= 1e-3
