@@ -1,0 +1,274 @@
+"""Benchmark: one tile-sparse video attention layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3a]
+
+A step is one whole layer over one batch of synthetic input already resident
+in HBM: tile map + gather, tile scores, top-k selection and the sparse
+attention, all in the library's kernels. Prints ONE JSON line.
+
+value = effective TFLOP/s of the whole layer (4*d * real query-key pairs the
+attention visits / step time). The roofline object covers the dominant
+kernel (the bf16 attention), timed with events on the stream it runs on.
+The CPU baseline is the oracle on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="3a")
+    ap.add_argument("--also", default="3b", help="extra workloads reported beside, ',' list")
+    ap.add_argument("--dense-steps", type=int, default=2)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-attn-only", action="store_true",
+                    help="run only warmup+steps of the layer (for profilers)")
+    return ap.parse_args()
+
+
+class Case:
+    """Library buffers and inputs for one workload, resident on the GPU."""
+
+    def __init__(self, wname: str, sparsity=None):
+        import numpy as np
+        import torch
+        from block_sparse_video_map_amd import vsa
+        from workloads import WORKLOADS
+        from workloads.inputs import make_qkv, make_weights
+        w = WORKLOADS[wname]
+        self.w = w
+        self.sparsity = w.sparsity if sparsity is None else sparsity
+        self.prob = vsa.Problem(w.B, w.H, w.d, w.grid, w.prefix, w.tile_shapes, w.dtype)
+        mode = vsa.VSA_SCORE_MEAN_GATE if w.scorer == "mean_gate" else vsa.VSA_SCORE_TRIPPOOL
+        proj = w.d if w.scorer == "mean_gate" else w.proj_dim
+        self.layer = vsa.Layer(self.prob, self.sparsity, mode, proj, with_lse=False)
+        t0 = time.time()
+        bits = w.dtype == "bf16"
+        q, k, v = make_qkv(w, as_bf16_bits=bits)
+        dev = [torch.from_numpy(x).cuda() for x in (q, k, v)]
+        del q, k, v
+        if bits:
+            dev = [x.view(torch.bfloat16) for x in dev]
+        self.q, self.k, self.v = dev
+        W = make_weights(w)
+        if w.scorer == "mean_gate":
+            self.wq, self.wk = torch.from_numpy(W["gate"]).cuda(), None
+        else:
+            self.wq = torch.from_numpy(W["proj_q"]).cuda()
+            self.wk = torch.from_numpy(W["proj_k"]).cuda()
+        torch.cuda.synchronize()
+        log(f"[bench] {wname}: inputs ready in {time.time() - t0:.1f}s")
+        self._np = np
+
+    def step(self):
+        self.layer.forward(self.q, self.k, self.v, self.wq, self.wk)
+
+    def flops(self) -> float:
+        """Effective FLOPs of the attention on this case's selection."""
+        import torch
+        from block_sparse_video_map_amd import vsa
+        self.step()
+        torch.cuda.synchronize()
+        s2t = self.layer.slot_to_token.cpu().numpy()
+        kv = None if self.sparsity == 0.0 else self.layer.kv_idx.cpu().numpy()
+        return vsa.vsa_count_flops(self.prob, self.sparsity, s2t, kv)
+
+    def time_steps(self, steps: int, warmup: int):
+        import torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
+
+    def stage_times(self, reps: int):
+        """Median ms per stage, from events on the launch stream."""
+        import torch
+        L = self.layer
+        names = ["map_gather", "scores", "select", "attention"]
+        fns = [lambda: L.map_tiles(self.q, self.k, self.v),
+               lambda: L.tile_scores(self.wq, self.wk),
+               L.select, L.attend]
+        if self.sparsity == 0.0:
+            names, fns = [names[0], names[3]], [fns[0], fns[3]]
+        samples = {n: [] for n in names}
+        for _ in range(reps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+            ev[0].record()
+            for i, f in enumerate(fns):
+                f()
+                ev[i + 1].record()
+            torch.cuda.synchronize()
+            for i, n in enumerate(names):
+                samples[n].append(ev[i].elapsed_time(ev[i + 1]))
+        med = {n: float(sorted(v)[len(v) // 2]) for n, v in samples.items()}
+        mean = {n: float(sum(v) / len(v)) for n, v in samples.items()}
+        return med, mean
+
+    def release(self):
+        import torch
+        del self.layer, self.q, self.k, self.v
+        torch.cuda.empty_cache()
+
+
+def cpu_baseline(wname: str, budget_s: float):
+    """The oracle, as it stands, on a bounded sample of the workload: head 0's
+    map, gather, pooling, scores and selection, then attention for as many
+    video query tiles (plus every prefix query tile) as fit the time budget.
+    Reported as effective TFLOP/s of the sampled attention over the whole
+    sampled time."""
+    import numpy as np
+
+    import oracle
+    from workloads import WORKLOADS
+    from workloads.inputs import head_qkv, make_weights
+    w = WORKLOADS[wname]
+    q, k, v = head_qkv(w, 0, 0)
+    W = make_weights(w)
+    shape = w.tile_shapes[0]
+    wq = W["gate"][0] if w.scorer == "mean_gate" else W["proj_q"][0]
+    wk = None if w.scorer == "mean_gate" else W["proj_k"][0]
+    t0 = time.perf_counter()
+    r = oracle.head_forward(q, k, v, w.grid, w.prefix, shape, w.sparsity, w.scorer, wq, wk,
+                            query_tiles=[])
+    tm, allow = r["tmap"], r["allow"]
+    order = list(range(tm.n_prefix_tiles)) + list(
+        np.random.default_rng(0).permutation(np.arange(tm.n_prefix_tiles, tm.n_tiles)))
+    real = tm.valid().sum(axis=1).astype(np.int64)
+    done_flops, n_tiles = 0, 0
+    scale = 1.0 / np.sqrt(w.d)
+    for tq in order:
+        oracle.sparse_attention(q, k, v, tm, allow, scale, query_tiles=[tq])
+        done_flops += 4 * w.d * int(real[tq]) * int(allow[tq].astype(np.int64) @ real)
+        n_tiles += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    return {"value": done_flops / el / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": (f"workload {wname}, head 0 of {w.H}: full map/gather/pool/score/select "
+                       f"plus float64 attention of {n_tiles} of {tm.n_tiles} query tiles "
+                       f"(prefix tiles first, then random video tiles) in {el:.1f}s"),
+            "seconds": round(el, 2), "host_cpus": os.cpu_count()}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {a.gpus}); the path shards by head "
+              "across GPUs with no exchange, which this build does not launch.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    from block_sparse_video_map_amd import vsa
+    from workloads import WORKLOADS
+
+    w = WORKLOADS[a.workload]
+    case = Case(a.workload)
+    flops = case.flops()
+    if a.profile_attn_only:
+        case.time_steps(a.steps, a.warmup)
+        log("[bench] profile run done")
+        return
+    ms_step = case.time_steps(a.steps, a.warmup) * 1e3
+    med, mean = case.stage_times(max(5, a.steps))
+    kept, frac = vsa.vsa_kept_stats(case.prob, case.sparsity)
+    attn_ms = mean["attention"]
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    log(f"[bench] {a.workload}: {ms_step:.3f} ms/step, attention {attn_ms:.3f} ms, "
+        f"{achieved:.1f} TFLOP/s on kept tiles")
+    case.release()
+
+    dense = Case(a.workload, sparsity=0.0)
+    dense_flops = dense.flops()
+    dense_ms = dense.time_steps(max(1, a.dense_steps), 1) * 1e3
+    dmed, dmean = dense.stage_times(max(1, a.dense_steps))
+    dense.release()
+    log(f"[bench] dense: {dense_ms:.2f} ms/step")
+
+    extra = {}
+    for name in [x for x in a.also.split(",") if x]:
+        c = Case(name)
+        f = c.flops()
+        ms = c.time_steps(max(3, a.steps // 2), 2) * 1e3
+        m2, mn2 = c.stage_times(5)
+        extra[name] = {"ms_per_step": round(ms, 4), "effective_tflops_layer": f / ms / 1e9,
+                       "attention_ms": round(mn2["attention"], 4),
+                       "effective_tflops_attention": f / mn2["attention"] / 1e9,
+                       "effective_tflop": f / 1e12, "stage_ms_median": m2}
+        c.release()
+        log(f"[bench] {name}: {ms:.3f} ms/step")
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle, bounded sample)")
+        cpu = cpu_baseline(a.workload, a.cpu_seconds)
+
+    T, Hv, Wv = w.grid
+    line = {
+        "metric": "effective TFLOP/s on kept tiles + ms/layer at ~105k tokens, "
+                  "75% sparsity, 1 GPU",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) + low-frequency 3D sinusoid per channel; "
+                "random N(0,1/d) gates)",
+        "config": {"workload": f"{a.workload}: {w.name}", "B": w.B, "H": w.H, "d": w.d,
+                   "video_grid": [T, Hv, Wv], "prefix": list(w.prefix),
+                   "tokens": w.N, "tile_shapes": [list(s) for s in w.tile_shapes],
+                   "scorer": w.scorer, "sparsity": w.sparsity},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_bf16_kernel<128>",
+                     "per_launch_flop": flops, "avg_launch_ms": round(attn_ms, 4)},
+        "cpu_baseline": cpu,
+        "effective_tflop_per_layer": flops / 1e12,
+        "attention_ms": round(attn_ms, 4),
+        "stage_ms_median": med,
+        "stage_ms_mean": mean,
+        "kept_tile_pairs": kept, "kept_fraction_of_full": round(frac, 5),
+        "dense": {"ms_per_step": round(dense_ms, 3), "attention_ms": round(dmean["attention"], 3),
+                  "effective_tflop": dense_flops / 1e12,
+                  "effective_tflops_attention": dense_flops / dmean["attention"] / 1e9},
+        "speedup_vs_dense_layer": round(dense_ms / ms_step, 3),
+        "also": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
