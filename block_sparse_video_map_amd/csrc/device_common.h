@@ -67,6 +67,20 @@ __device__ inline int32_t slot_token(const Plan &p, int s, int tile, int slot) {
   return p.P + (t * p.Hv + y) * p.Wv + x;
 }
 
+// Buffer resource over `bytes` bytes at `base` (raw, untyped loads; reads past
+// the end return zero instead of faulting). The varying part of an address
+// then lives in SGPRs (soffset) plus one per-lane VGPR offset.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ inline bf16x8 buffer_load16(__amdgpu_buffer_rsrc_t r, int voffset, int soffset) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voffset, soffset, 0);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 __device__ inline float bf16_to_float(bf16_bits u) {
   return __uint_as_float(((uint32_t)u) << 16);
 }
