@@ -3,8 +3,8 @@
 // Pooling runs one workgroup per (video tile, batch*head, Q|K): the tile is
 // read once from the tiled layout into LDS, reduced over its real slots in
 // double, and projected (mean gate) or projected-then-reduced (TripPool).
-// Scoring is a double-precision GEMM per head, 64x64 outputs per workgroup,
-// rounded once to float on the way out.
+// Scoring is a double-precision GEMM per head on the f64 MFMA, 64x64 outputs
+// per workgroup, rounded once to float on the way out.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -45,25 +45,30 @@ __global__ __launch_bounds__(256) void pool_mean_gate_kernel(
   load_tile_f32<T, D, LD>(src, xs);
   __syncthreads();
 
+  // Four independent partial sums per channel / output keep the double adds
+  // and FMAs from forming one long dependency chain.
   if (threadIdx.x < D) {
     const int c = threadIdx.x;
-    double sum = 0.0;
+    double part[4] = {0.0, 0.0, 0.0, 0.0};
     int n = 0;
+#pragma unroll 4
     for (int sl = 0; sl < kTile; ++sl) {
       if (valid[sl]) {
-        sum += (double)xs[sl * LD + c];
+        part[sl % 4] += (double)xs[sl * LD + c];
         ++n;
       }
     }
-    mean[c] = sum / (double)n;
+    mean[c] = ((part[0] + part[1]) + (part[2] + part[3])) / (double)n;
   }
   __syncthreads();
 
   if (threadIdx.x < D) {
     const int j = threadIdx.x;
-    double acc = 0.0;
-    for (int c = 0; c < D; ++c) acc = fma(mean[c], (double)w[c * D + j], acc);
-    pooled[(((int64_t)which * p.B * p.H + bh) * p.max_vt + vt_i) * D + j] = acc;
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+    for (int c = 0; c < D; ++c) acc[c % 4] = fma(mean[c], (double)w[c * D + j], acc[c % 4]);
+    pooled[(((int64_t)which * p.B * p.H + bh) * p.max_vt + vt_i) * D + j] =
+        (acc[0] + acc[1]) + (acc[2] + acc[3]);
   }
 }
 
@@ -133,62 +138,74 @@ __global__ __launch_bounds__(256) void pool_trippool_kernel(
   }
 }
 
-// s[bh][i][j] = <Qdesc_i, Kdesc_j>, double accumulation, one float rounding.
+// s[bh][i][j] = <Qdesc_i, Kdesc_j>: a double-precision GEMM per head on the
+// 16x16x4 f64 MFMA, rounded once to float on the way out. A workgroup owns a
+// 64x64 block of scores, each of its four waves a 32x32 quarter (2x2 MFMA
+// blocks). Per 16-wide slice of the descriptor, lane l loads four consecutive
+// doubles of its row at offset 4*(l/16): MFMA m then contracts channel
+// k0 + 4*(l/16) + m of both operands, so the four products cover the slice.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 constexpr int kSB = 64;   // output block edge
-constexpr int kSK = 32;   // reduction chunk
 
 __global__ __launch_bounds__(256) void scores_kernel(Plan p, int r,
                                                      const double *__restrict__ pooled,
                                                      float *__restrict__ scores) {
-  __shared__ double As[kSB][kSK + 1];
-  __shared__ double Bs[kSB][kSK + 1];
   const int bh = blockIdx.z, h = bh % p.H, s = h % p.n_shapes;
   const int n = p.n_vt[s];
   const int i0 = blockIdx.y * kSB, j0 = blockIdx.x * kSB;
   if (i0 >= n || j0 >= n) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int lane = threadIdx.x % 64, g = lane / 16, l16 = lane % 16;
+  const int wi = i0 + (wave / 2) * 32, wj = j0 + (wave % 2) * 32;
   const double *Qd = pooled + (int64_t)bh * p.max_vt * r;
   const double *Kd = pooled + ((int64_t)p.B * p.H + bh) * p.max_vt * r;
-  const int ty = threadIdx.x / 16, tx = threadIdx.x % 16;
 
-  double acc[4][4];
+  int ra[2], rb[2];
+  bool va[2], vb[2];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
-
-  for (int k0 = 0; k0 < r; k0 += kSK) {
-    for (int e = threadIdx.x; e < kSB * kSK; e += blockDim.x) {
-      int row = e / kSK, kk = e % kSK;
-      bool kin = k0 + kk < r;
-      As[row][kk] = (i0 + row < n && kin) ? Qd[(int64_t)(i0 + row) * r + k0 + kk] : 0.0;
-      Bs[row][kk] = (j0 + row < n && kin) ? Kd[(int64_t)(j0 + row) * r + k0 + kk] : 0.0;
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int kk = 0; kk < kSK; ++kk) {
-      double av[4], bv[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) av[a] = As[ty + 16 * a][kk];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) bv[b] = Bs[tx + 16 * b][kk];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = fma(av[a], bv[b], acc[a][b]);
-    }
-    __syncthreads();
+  for (int a = 0; a < 2; ++a) {
+    ra[a] = wi + a * 16 + l16;
+    rb[a] = wj + a * 16 + l16;
+    va[a] = ra[a] < n;
+    vb[a] = rb[a] < n;
   }
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = (f64x4){0.0, 0.0, 0.0, 0.0};
+
+  for (int k0 = 0; k0 < r; k0 += 16) {
+    const int kk = k0 + 4 * g;          // r is a multiple of 4: groups are all-in or all-out
+    double av[2][4], bv[2][4];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const bool oka = va[a] && kk < r, okb = vb[a] && kk < r;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        av[a][m] = oka ? Qd[(int64_t)ra[a] * r + kk + m] : 0.0;
+        bv[a][m] = okb ? Kd[(int64_t)rb[a] * r + kk + m] : 0.0;
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a][m], bv[b][m], acc[a][b], 0, 0, 0);
+  }
+  // D element e of lane l is row 4*e + l/16, column l % 16 of the block.
   float *out = scores + (int64_t)bh * p.max_vt * p.max_vt;
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    int i = i0 + ty + 16 * a;
-    if (i >= n) continue;
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      int j = j0 + tx + 16 * b;
-      if (j < n) out[(int64_t)i * p.max_vt + j] = (float)acc[a][b];
-    }
-  }
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = wi + a * 16 + 4 * e + g, j = wj + b * 16 + l16;
+        if (i < n && j < n) out[(int64_t)i * p.max_vt + j] = (float)acc[a][b][e];
+      }
 }
 
 template <typename T, int D>

@@ -1,10 +1,13 @@
 // Step 3: top-k video key tiles per video query tile.
 //
-// One workgroup per score row. The row is loaded into LDS as 64-bit keys
-// (order-preserving float bits << 32 | ~index), bitonic-sorted descending in
-// LDS, so the first k keys are the k best tiles with ties going to the lower
-// index. The kept tiles are flagged and compacted in index order with wave
-// ballots, which gives the ascending block-index list directly.
+// One workgroup per score row. Scores become order-preserving 32-bit keys
+// (larger key = larger score, -0.0 folded into +0.0) held in registers, each
+// thread owning a contiguous run of indices. A most-significant-digit radix
+// select (four 8-bit passes with LDS histograms) finds the k-th largest key T
+// and how many keys equal to T are kept; ties keep the lowest indices. A
+// single ordered pass then flags "key > T, or key == T among the first ties"
+// and compacts the flagged indices with block prefix sums, which yields the
+// ascending block-index list directly. O(n) work per row, exact.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -12,77 +15,118 @@ namespace vsa {
 namespace {
 
 constexpr int kSelThreads = 256;
+constexpr int kSelWaves = kSelThreads / 64;
 
-__device__ inline uint64_t sort_key(float x, uint32_t idx) {
-  if (x == 0.0f) x = 0.0f;                    // -0.0 ranks equal to +0.0
+__device__ inline uint32_t order_key(float x) {
+  if (x == 0.0f) x = 0.0f;                     // -0.0 ranks equal to +0.0
   uint32_t u = __float_as_uint(x);
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - idx);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int PMAX>
+// Exclusive block scan of one int per thread; also returns the block total.
+__device__ inline int block_exclusive_scan(int v, int *wave_tot, int &total) {
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    if (w < wave) base += wave_tot[w];
+    total += wave_tot[w];
+  }
+  __syncthreads();
+  return base + incl - v;
+}
+
+// E = keys per thread (n <= E * kSelThreads).
+template <int E>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(Plan p,
                                                              const float *__restrict__ scores,
                                                              int32_t *__restrict__ kv_idx) {
-  __shared__ uint64_t keys[PMAX];
-  __shared__ uint8_t flag[PMAX];
-  __shared__ int wave_cnt[kSelThreads / 64];
+  __shared__ int hist[256];
+  __shared__ int wave_tot[kSelWaves];
+  __shared__ int sel_bin, sel_above;
 
   const int i = blockIdx.x, bh = blockIdx.y, h = bh % p.H, s = h % p.n_shapes;
   const int n = p.n_vt[s];
   if (i >= n) return;
   const int k = p.k[s];
-  int P2 = 1;
-  while (P2 < n) P2 <<= 1;
+  const int t = threadIdx.x;
+  const int j0 = t * E;                         // this thread's first index
 
   const float *row = scores + ((int64_t)bh * p.max_vt + i) * p.max_vt;
-  for (int j = threadIdx.x; j < P2; j += kSelThreads) {
-    keys[j] = j < n ? sort_key(row[j], (uint32_t)j) : 0ull;
-    flag[j] = 0;
-  }
-  __syncthreads();
+  uint32_t key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) key[e] = (j0 + e < n) ? order_key(row[j0 + e]) : 0u;
 
-  // Bitonic sort, descending.
-  for (int size = 2; size <= P2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = threadIdx.x; t < P2 / 2; t += kSelThreads) {
-        int lo = 2 * stride * (t / stride) + (t % stride);
-        int hi = lo + stride;
-        uint64_t a = keys[lo], b = keys[hi];
-        bool desc = (lo & size) == 0;
-        if (desc ? (a < b) : (a > b)) {
-          keys[lo] = b;
-          keys[hi] = a;
-        }
+  // Radix select of the k-th largest key: prefix/need narrow digit by digit.
+  uint32_t prefix = 0, pmask = 0;
+  int need = k;
+#pragma unroll 1
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[t] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (j0 + e < n && (key[e] & pmask) == prefix) atomicAdd(&hist[(key[e] >> shift) & 255], 1);
+    __syncthreads();
+    // Counts from the top bin down: thread t looks at bin 255 - t.
+    const int c = hist[255 - t];
+    int total;
+    const int above = block_exclusive_scan(c, wave_tot, total);   // keys in higher bins
+    if (above < need && need <= above + c) {
+      sel_bin = 255 - t;
+      sel_above = above;
+    }
+    __syncthreads();
+    need -= sel_above;
+    prefix |= (uint32_t)sel_bin << shift;
+    pmask |= 255u << shift;
+    __syncthreads();
+  }
+  const uint32_t T = prefix;                    // k-th largest key; keep `need` ties
+
+  // Ordered compaction: ties are ranked by index among themselves.
+  int n_eq = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) n_eq += (j0 + e < n && key[e] == T);
+  int tot_eq;
+  int eq_rank = block_exclusive_scan(n_eq, wave_tot, tot_eq);
+  int n_keep = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (j0 + e < n) {
+      if (key[e] > T) {
+        ++n_keep;
+      } else if (key[e] == T) {
+        n_keep += eq_rank < need;
+        ++eq_rank;
       }
-      __syncthreads();
     }
   }
-
-  for (int t = threadIdx.x; t < k; t += kSelThreads)
-    flag[0xFFFFFFFFu - (uint32_t)(keys[t] & 0xFFFFFFFFull)] = 1;
-  __syncthreads();
-
-  // Ordered compaction of the flagged indices.
+  int tot_keep;
+  int pos = block_exclusive_scan(n_keep, wave_tot, tot_keep);   // tot_keep == k
   int32_t *out = kv_idx + ((int64_t)bh * p.max_vt + i) * p.k_max;
-  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-  int base = 0;
-  for (int c0 = 0; c0 < n; c0 += kSelThreads) {
-    int j = c0 + threadIdx.x;
-    bool f = j < n && flag[j];
-    uint64_t m = __ballot(f);
-    int before = __popcll(m & ((1ull << lane) - 1ull));
-    if (lane == 0) wave_cnt[wave] = __popcll(m);
-    __syncthreads();
-    int off = base;
-    for (int w = 0; w < wave; ++w) off += wave_cnt[w];
-    if (f) out[off + before] = j;
-    int total = 0;
-    for (int w = 0; w < kSelThreads / 64; ++w) total += wave_cnt[w];
-    base += total;
-    __syncthreads();
+  eq_rank -= n_eq;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (j0 + e < n) {
+      bool keep = key[e] > T;
+      if (key[e] == T) {
+        keep = eq_rank < need;
+        ++eq_rank;
+      }
+      if (keep) out[pos++] = j0 + e;
+    }
   }
-  for (int t = k + threadIdx.x; t < p.k_max; t += kSelThreads) out[t] = -1;
+  for (int c = k + t; c < p.k_max; c += kSelThreads) out[c] = -1;
 }
 
 }  // namespace
@@ -92,13 +136,14 @@ hipError_t launch_select(const Plan &p, const float *scores, int32_t *kv_idx,
                          hipStream_t stream) {
   dim3 grid(p.max_vt, p.B * p.H);
   dim3 block(vsa::kSelThreads);
-  if (p.max_vt <= 1024)
-    hipLaunchKernelGGL(vsa::select_kernel<1024>, grid, block, 0, stream, p, scores, kv_idx);
-  else if (p.max_vt <= 2048)
-    hipLaunchKernelGGL(vsa::select_kernel<2048>, grid, block, 0, stream, p, scores, kv_idx);
-  else if (p.max_vt <= 4096)
-    hipLaunchKernelGGL(vsa::select_kernel<4096>, grid, block, 0, stream, p, scores, kv_idx);
+  const int e = (p.max_vt + vsa::kSelThreads - 1) / vsa::kSelThreads;
+  if (e <= 4)
+    hipLaunchKernelGGL(vsa::select_kernel<4>, grid, block, 0, stream, p, scores, kv_idx);
+  else if (e <= 8)
+    hipLaunchKernelGGL(vsa::select_kernel<8>, grid, block, 0, stream, p, scores, kv_idx);
+  else if (e <= 16)
+    hipLaunchKernelGGL(vsa::select_kernel<16>, grid, block, 0, stream, p, scores, kv_idx);
   else
-    hipLaunchKernelGGL(vsa::select_kernel<8192>, grid, block, 0, stream, p, scores, kv_idx);
+    hipLaunchKernelGGL(vsa::select_kernel<32>, grid, block, 0, stream, p, scores, kv_idx);
   return hipGetLastError();
 }

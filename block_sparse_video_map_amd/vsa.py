@@ -16,7 +16,8 @@ from dataclasses import dataclass
 from typing import Optional, Sequence, Tuple
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libvsa.so")
+# VSA_LIBRARY names another build of the same library (e.g. a tuning build).
+LIB_PATH = os.environ.get("VSA_LIBRARY") or os.path.join(_PKG, "libvsa.so")
 
 VSA_OK, VSA_ERR_INVALID_ARG, VSA_ERR_UNSUPPORTED, VSA_ERR_SIZE, VSA_ERR_HIP = 0, -1, -2, -3, -4
 VSA_F32, VSA_BF16 = 0, 1
