@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-attn-only", action="store_true",
                     help="run only warmup+steps of the layer (for profilers)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="with --profile-attn-only: also run one plain device copy of this "
+                         "many MiB (reference for the memory-traffic counters)")
     return ap.parse_args()
 
 
@@ -198,6 +201,12 @@ def main():
     flops = case.flops()
     if a.profile_attn_only:
         case.time_steps(a.steps, a.warmup)
+        if a.copy_calibration_mib:
+            n = a.copy_calibration_mib * (1 << 20) // 4
+            src = torch.ones(n, dtype=torch.float32, device="cuda")
+            dst = torch.empty_like(src)
+            dst.copy_(src)
+            torch.cuda.synchronize()
         log("[bench] profile run done")
         return
     ms_step = case.time_steps(a.steps, a.warmup) * 1e3

@@ -23,7 +23,11 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libvsa.so")
 
 SOURCES = ["plan.cpp", "abi.hip", "map_gather.hip", "pool_score.hip", "select.hip",
-           "attn_bf16.hip", "attn_bf16_lds.hip", "attn_f32.hip"]
+           "attn_bf16.hip", "attn_f32.hip"]
+# Per-source extra flags. The attention kernel keeps all 64 queries of a tile
+# in one wave; with MFMA results forced into VGPRs the register allocator
+# keeps its working set out of scratch (AGPRs only serve as spill space).
+EXTRA = {"attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 
@@ -45,7 +49,8 @@ def common_flags():
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc()] + common_flags() + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ([hipcc()] + common_flags() + EXTRA.get(src, []) + lang
+           + ["-c", os.path.join(CSRC, src), "-o", obj])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -1,7 +1,6 @@
 // The C-ABI entry points: validate on the host, then enqueue the kernels.
 #include <cmath>
 #include <cstdint>
-#include <cstdlib>
 
 #include "kernels.h"
 #include "plan.h"
@@ -10,34 +9,16 @@ namespace vsa {
 hipError_t launch_attn_bf16(const Plan &p, const void *qt, const void *kt, const void *vt,
                             const int32_t *s2t, const int32_t *kv_idx, float scale,
                             void *out, float *lse, hipStream_t stream);
-hipError_t launch_attn_bf16_lds(const Plan &p, const void *qt, const void *kt, const void *vt,
-                                const int32_t *s2t, const int32_t *kv_idx, float scale,
-                                void *out, float *lse, hipStream_t stream);
 hipError_t launch_attn_f32(const Plan &p, const void *qt, const void *kt, const void *vt,
                            const int32_t *s2t, const int32_t *kv_idx, float scale,
                            void *out, float *lse, hipStream_t stream);
 }  // namespace vsa
 
-namespace {
-// bf16 attention kernel variant: 0 = K/V straight to registers, 1 = K/V
-// staged through LDS. VSA_ATTN_KERNEL overrides the default (tuning only).
-int attn_variant() {
-  static const int v = [] {
-    const char *e = getenv("VSA_ATTN_KERNEL");
-    return e ? atoi(e) : 0;
-  }();
-  return v;
-}
-}  // namespace
-
 hipError_t launch_attention(const Plan &p, const void *qt, const void *kt, const void *vt,
                             const int32_t *s2t, const int32_t *kv_idx, float scale,
                             void *out, float *lse, hipStream_t stream) {
-  if (p.dtype == VSA_BF16) {
-    if (attn_variant() == 1)
-      return vsa::launch_attn_bf16_lds(p, qt, kt, vt, s2t, kv_idx, scale, out, lse, stream);
+  if (p.dtype == VSA_BF16)
     return vsa::launch_attn_bf16(p, qt, kt, vt, s2t, kv_idx, scale, out, lse, stream);
-  }
   return vsa::launch_attn_f32(p, qt, kt, vt, s2t, kv_idx, scale, out, lse, stream);
 }
 

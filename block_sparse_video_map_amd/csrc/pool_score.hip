@@ -73,17 +73,24 @@ __global__ __launch_bounds__(256) void pool_mean_gate_kernel(
 }
 
 // Veda TripPool: project every real token (d -> R), then [Avg | Max | Min].
+// The projection X[64 tokens x D] . P[D x R] runs on the 16x16x4 f64 MFMA:
+// wave w owns tokens 16w..16w+15 and all R columns (16-column blocks). Lane
+// l reads four consecutive channels k0 + 4*(l/16) + m of its token row and of
+// its column of P (transposed in LDS), MFMA m contracting channel m of that
+// group. Each lane then holds four tokens (rows 4e + l/16) of one column
+// (l % 16); the statistics are reduced across lanes, then across waves.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
 template <typename T, int D, int R>
 __global__ __launch_bounds__(256) void pool_trippool_kernel(
     Plan p, const T *__restrict__ qt, const T *__restrict__ kt,
     const int32_t *__restrict__ s2t, const float *__restrict__ wq,
     const float *__restrict__ wk, double *__restrict__ pooled) {
-  constexpr int LD = D + 1;
-  constexpr int G = 256 / R;          // token groups
-  constexpr int TPT = kTile / G;      // tokens per thread
-  __shared__ float xs[kTile * LD];
-  __shared__ float ws[D * R];
-  __shared__ double red_sum[G * R], red_max[G * R], red_min[G * R];
+  constexpr int LD = D + 4;                  // float rows, 16-byte aligned
+  constexpr int RB = (R + 15) / 16;          // 16-column blocks
+  __shared__ __attribute__((aligned(16))) float xs[kTile * LD];
+  __shared__ __attribute__((aligned(16))) float pt[RB * 16 * LD];   // P transposed
+  __shared__ double red[3][4][RB * 16];      // [stat][wave][column]
   __shared__ int valid[kTile];
 
   const int vt_i = blockIdx.x, bh = blockIdx.y, which = blockIdx.z;
@@ -95,41 +102,73 @@ __global__ __launch_bounds__(256) void pool_trippool_kernel(
 
   if (threadIdx.x < kTile)
     valid[threadIdx.x] = s2t[((int64_t)s * p.max_tiles + tile) * kTile + threadIdx.x] >= 0;
-  for (int i = threadIdx.x; i < D * R; i += blockDim.x) ws[i] = w[i];
+  for (int i = threadIdx.x; i < RB * 16 * D; i += blockDim.x) {
+    const int c = i % D, j = i / D;          // pt[j][c] = P[c][j], zero past R
+    pt[j * LD + c] = j < R ? w[c * R + j] : 0.f;
+  }
   load_tile_f32<T, D, LD>(src, xs);
   __syncthreads();
 
-  const int j = threadIdx.x % R, g = threadIdx.x / R;
-  double acc[TPT];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int lane = threadIdx.x % 64, g = lane / 16, l16 = lane % 16;
+  f64x4 acc[RB];
 #pragma unroll
-  for (int t = 0; t < TPT; ++t) acc[t] = 0.0;
-  for (int c = 0; c < D; ++c) {
-    const double wc = (double)ws[c * R + j];
+  for (int b = 0; b < RB; ++b) acc[b] = (f64x4){0.0, 0.0, 0.0, 0.0};
+  const float *xrow = xs + (wave * 16 + l16) * LD;
+#pragma unroll 2
+  for (int k0 = 0; k0 < D; k0 += 16) {
+    const int kk = k0 + 4 * g;
+    const float4 xa = *reinterpret_cast<const float4 *>(xrow + kk);
+    const double a4[4] = {xa.x, xa.y, xa.z, xa.w};
+    double b4[RB][4];
 #pragma unroll
-    for (int t = 0; t < TPT; ++t) acc[t] = fma((double)xs[(g + t * G) * LD + c], wc, acc[t]);
+    for (int b = 0; b < RB; ++b) {
+      const float4 pb = *reinterpret_cast<const float4 *>(pt + (b * 16 + l16) * LD + kk);
+      b4[b][0] = pb.x; b4[b][1] = pb.y; b4[b][2] = pb.z; b4[b][3] = pb.w;
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int b = 0; b < RB; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(a4[m], b4[b][m], acc[b], 0, 0, 0);
   }
-  double sum = 0.0, mx = -INFINITY, mn = INFINITY;
+
+  // Element e of lane l: token wave*16 + 4e + l/16, column b*16 + l%16.
 #pragma unroll
-  for (int t = 0; t < TPT; ++t) {
-    if (valid[g + t * G]) {
-      sum += acc[t];
-      mx = fmax(mx, acc[t]);
-      mn = fmin(mn, acc[t]);
+  for (int b = 0; b < RB; ++b) {
+    double sum = 0.0, mx = -INFINITY, mn = INFINITY;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (valid[wave * 16 + 4 * e + g]) {
+        sum += acc[b][e];
+        mx = fmax(mx, acc[b][e]);
+        mn = fmin(mn, acc[b][e]);
+      }
+    }
+#pragma unroll
+    for (int d = 16; d < 64; d <<= 1) {      // the four lanes of a column
+      sum += __shfl_xor(sum, d);
+      mx = fmax(mx, __shfl_xor(mx, d));
+      mn = fmin(mn, __shfl_xor(mn, d));
+    }
+    if (g == 0) {
+      red[0][wave][b * 16 + l16] = sum;
+      red[1][wave][b * 16 + l16] = mx;
+      red[2][wave][b * 16 + l16] = mn;
     }
   }
-  red_sum[g * R + j] = sum;
-  red_max[g * R + j] = mx;
-  red_min[g * R + j] = mn;
   __syncthreads();
 
   if (threadIdx.x < R) {
+    const int j = threadIdx.x;
     int n = 0;
     for (int sl = 0; sl < kTile; ++sl) n += valid[sl];
     double ts = 0.0, tx = -INFINITY, tn = INFINITY;
-    for (int gg = 0; gg < G; ++gg) {
-      ts += red_sum[gg * R + j];
-      tx = fmax(tx, red_max[gg * R + j]);
-      tn = fmin(tn, red_min[gg * R + j]);
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      ts += red[0][ww][j];
+      tx = fmax(tx, red[1][ww][j]);
+      tn = fmin(tn, red[2][ww][j]);
     }
     double *out = pooled + (((int64_t)which * p.B * p.H + bh) * p.max_vt + vt_i) * (3 * R);
     out[j] = ts / (double)n;
@@ -144,7 +183,6 @@ __global__ __launch_bounds__(256) void pool_trippool_kernel(
 // blocks). Per 16-wide slice of the descriptor, lane l loads four consecutive
 // doubles of its row at offset 4*(l/16): MFMA m then contracts channel
 // k0 + 4*(l/16) + m of both operands, so the four products cover the slice.
-typedef double f64x4 __attribute__((ext_vector_type(4)));
 constexpr int kSB = 64;   // output block edge
 
 __global__ __launch_bounds__(256) void scores_kernel(Plan p, int r,
@@ -175,25 +213,38 @@ __global__ __launch_bounds__(256) void scores_kernel(Plan p, int r,
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = (f64x4){0.0, 0.0, 0.0, 0.0};
 
-  for (int k0 = 0; k0 < r; k0 += 16) {
+  // Operands of one 16-wide slice: av/bv[buffer][block][m]; the next slice is
+  // fetched while the current one is multiplied.
+  double av[2][2][4], bv[2][2][4];
+  auto fetch = [&](int buf, int k0) {
     const int kk = k0 + 4 * g;          // r is a multiple of 4: groups are all-in or all-out
-    double av[2][4], bv[2][4];
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       const bool oka = va[a] && kk < r, okb = vb[a] && kk < r;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        av[a][m] = oka ? Qd[(int64_t)ra[a] * r + kk + m] : 0.0;
-        bv[a][m] = okb ? Kd[(int64_t)rb[a] * r + kk + m] : 0.0;
+        av[buf][a][m] = oka ? Qd[(int64_t)ra[a] * r + kk + m] : 0.0;
+        bv[buf][a][m] = okb ? Kd[(int64_t)rb[a] * r + kk + m] : 0.0;
       }
     }
+  };
+  auto multiply = [&](int buf) {
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a][m], bv[b][m], acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[buf][a][m], bv[buf][b][m],
+                                                           acc[a][b], 0, 0, 0);
+  };
+  fetch(0, 0);
+  for (int k0 = 0; k0 < r; k0 += 32) {
+    if (k0 + 16 < r) fetch(1, k0 + 16);
+    multiply(0);
+    if (k0 + 16 >= r) break;
+    if (k0 + 32 < r) fetch(0, k0 + 32);
+    multiply(1);
   }
   // D element e of lane l is row 4*e + l/16, column l % 16 of the block.
   float *out = scores + (int64_t)bh * p.max_vt * p.max_vt;
