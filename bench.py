@@ -38,7 +38,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="3a")
-    ap.add_argument("--also", default="3b", help="extra workloads reported beside, ',' list")
+    ap.add_argument("--also", default="3b,3a-h3",
+                    help="extra workloads reported beside, ',' list; a '-h3' suffix keeps "
+                         "only heads 0-2 (one GPU's share of 24 heads over 8 GPUs)")
     ap.add_argument("--dense-steps", type=int, default=2)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -53,13 +55,17 @@ def parse():
 class Case:
     """Library buffers and inputs for one workload, resident on the GPU."""
 
-    def __init__(self, wname: str, sparsity=None):
+    def __init__(self, wname: str, sparsity=None, heads=None):
+        import dataclasses
+
         import numpy as np
         import torch
         from block_sparse_video_map_amd import vsa
         from workloads import WORKLOADS
         from workloads.inputs import make_qkv, make_weights
         w = WORKLOADS[wname]
+        if heads is not None:
+            w = dataclasses.replace(w, H=heads)
         self.w = w
         self.sparsity = w.sparsity if sparsity is None else sparsity
         self.prob = vsa.Problem(w.B, w.H, w.d, w.grid, w.prefix, w.tile_shapes, w.dtype)
@@ -131,6 +137,24 @@ class Case:
         med = {n: float(sorted(v)[len(v) // 2]) for n, v in samples.items()}
         mean = {n: float(sum(v) / len(v)) for n, v in samples.items()}
         return med, mean
+
+    def stage_bytes(self) -> dict:
+        """Algorithmic HBM bytes of the HBM-bound stages (each input read and
+        each output written once)."""
+        w, sz = self.w, self.layer.sizes
+        es = 2 if w.dtype == "bf16" else 4
+        ns = len(w.tile_shapes)
+        heads = [h % ns for h in range(w.H)]
+        tiles = sum(sz.n_tiles[s] for s in heads) * w.B
+        vt = sum(sz.n_video_tiles[s] for s in heads) * w.B
+        vt2 = sum(sz.n_video_tiles[s] ** 2 for s in heads) * w.B
+        kk = sum(sz.n_video_tiles[s] * sz.k[s] for s in heads) * w.B
+        r = w.d if w.scorer == "mean_gate" else 3 * w.proj_dim
+        out = {"map_gather": 3 * es * w.B * w.H * w.N * w.d + 3 * es * tiles * 64 * w.d}
+        if self.sparsity != 0.0:
+            out["scores"] = 2 * es * vt * 64 * w.d + 2 * 8 * vt * r + 4 * vt2
+            out["select"] = 4 * vt2 + 4 * kk
+        return out
 
     def release(self):
         import torch
@@ -212,6 +236,10 @@ def main():
     ms_step = case.time_steps(a.steps, a.warmup) * 1e3
     med, mean = case.stage_times(max(5, a.steps))
     kept, frac = vsa.vsa_kept_stats(case.prob, case.sparsity)
+    sbytes = case.stage_bytes()
+    stage_gbs = {n: {"bytes": b, "GB/s": round(b / (mean[n] * 1e-3) / 1e9, 1),
+                     "frac_of_hbm_peak": round(b / (mean[n] * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}
+                 for n, b in sbytes.items()}
     attn_ms = mean["attention"]
     achieved = flops / (attn_ms * 1e-3) / 1e12
     log(f"[bench] {a.workload}: {ms_step:.3f} ms/step, attention {attn_ms:.3f} ms, "
@@ -227,7 +255,12 @@ def main():
 
     extra = {}
     for name in [x for x in a.also.split(",") if x]:
-        c = Case(name)
+        heads = None
+        if name.endswith("-h3"):          # one GPU's share when 8 GPUs split the heads
+            name, heads = name[:-3], 3
+        c = Case(name, heads=heads)
+        if heads is not None:
+            name = f"{name}-h3"
         f = c.flops()
         ms = c.time_steps(max(3, a.steps // 2), 2) * 1e3
         m2, mn2 = c.stage_times(5)
@@ -244,6 +277,11 @@ def main():
         cpu = cpu_baseline(a.workload, a.cpu_seconds)
 
     T, Hv, Wv = w.grid
+    from block_sparse_video_map_amd.profsum import read_traffic
+    kname = "attn_bf16_kernel<128>" if w.d == 128 else "attn_bf16_kernel<64>"
+    rec = read_traffic(os.path.join(ROOT, "profiles", f"attn_bf16_{a.workload}_traffic.md"),
+                       "attn_bf16_kernel", a.workload)
+    traffic = rec["bytes_per_launch"] if rec else None
     line = {
         "metric": "effective TFLOP/s on kept tiles + ms/layer at ~105k tokens, "
                   "75% sparsity, 1 GPU",
@@ -261,14 +299,17 @@ def main():
                    "scorer": w.scorer, "sparsity": w.sparsity},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "attn_bf16_kernel<128>",
-                     "per_launch_flop": flops, "avg_launch_ms": round(attn_ms, 4)},
+                     "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "traffic_unit": "bytes per launch (HBM, scaled rocprofv3 counters)",
+                     "kernel": kname,
+                     "per_launch_flop": flops, "avg_launch_ms": round(attn_ms, 4),
+                     "tile_granular_flop": 4.0 * w.d * 64 * 64 * kept},
         "cpu_baseline": cpu,
         "effective_tflop_per_layer": flops / 1e12,
         "attention_ms": round(attn_ms, 4),
         "stage_ms_median": med,
         "stage_ms_mean": mean,
+        "stage_hbm": stage_gbs,
         "kept_tile_pairs": kept, "kept_fraction_of_full": round(frac, 5),
         "dense": {"ms_per_step": round(dense_ms, 3), "attention_ms": round(dmean["attention"], 3),
                   "effective_tflop": dense_flops / 1e12,
