@@ -24,10 +24,8 @@ LIB = os.path.join(PKG, "libvsa.so")
 
 SOURCES = ["plan.cpp", "abi.hip", "map_gather.hip", "pool_score.hip", "select.hip",
            "attn_bf16.hip", "attn_f32.hip"]
-# Per-source extra flags. The attention kernel keeps all 64 queries of a tile
-# in one wave; with MFMA results forced into VGPRs the register allocator
-# keeps its working set out of scratch (AGPRs only serve as spill space).
-EXTRA = {"attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source extra flags (none needed at present).
+EXTRA: dict = {}
 ARCH = "gfx950"
 
 

@@ -1,33 +1,40 @@
 // Step 4 (bf16): tile-skipping flash attention on the 32x32x16 bf16 MFMA.
 //
-// Work unit: one 64-token query tile per workgroup of four waves, one wave
-// per SIMD. The query tile's key-tile list (all prefix tiles, then its kept
-// video tiles; every tile for a prefix query tile) is dealt round-robin to
-// the four waves ("key splits"); every wave holds all 64 queries, so each
-// K/V byte it fetches serves 64 queries (no wave fetches what another one
-// fetches). Each wave keeps its own running max, sum and output; the four
-// splits are merged in LDS at the end.
+// Work unit: one 64-token query tile per workgroup of eight waves, two per
+// SIMD. The tile's key-tile list (all prefix tiles, then its kept video
+// tiles; every tile for a prefix query tile) is dealt round-robin to four
+// key splits; each split is served by two waves, one per 32-query half.
+// Every split keeps its own running max, sum and output; the four are merged
+// in LDS at the end. One query tile per CU keeps the key tiles that
+// neighbouring query tiles share close together in time, so that they hit
+// in the XCD's L2.
+//
+// The two waves of a split share each K/V tile through LDS: a 32-key half
+// ("unit") of a tile is copied from HBM straight into a two-slot LDS ring of
+// the split by direct-to-LDS buffer loads (wave 0 copies the K blocks, wave
+// 1 the V blocks; no registers held while in flight), one unit ahead of its
+// use. One workgroup barrier per unit orders "next slot landed" and "this
+// slot read by both waves". With two waves per SIMD the hardware overlaps
+// one wave's softmax (VALU) with the other's products (MFMA).
 //
 // The products are taken transposed, S^T = K Q^T and O^T = V^T P^T, so that
-// every lane owns one query column: the softmax max needs a single exchange
-// between the two 32-lane halves (v_permlane32_swap), the rescale of O is one
-// scalar per lane, and the accumulator of S^T is already the B operand of the
-// PV product once converted to bf16. Q/K tiles are stored in the MFMA operand
-// order and V tiles in the matching column order (see the tiled layouts), so
-// every operand fetch is a contiguous 1 KB wave load straight into registers
-// through a buffer resource whose tile offset stays in scalar registers.
+// every lane owns one query column: the S^T accumulator is already the B
+// operand of the PV product once converted to bf16, and a rescale of O is
+// one scalar per lane. Q/K tiles are stored in the MFMA operand order and V
+// tiles in the matching column order, so every operand block is a
+// contiguous 1 KB wave access.
 //
-// A wave walks its key tiles in 32-key halves ("units"); K and V of a unit
-// are fetched two units ahead into double buffers, and S of unit u+1 is
-// computed before the softmax of unit u. The running max is an integer in
-// log2 units and is only raised when a row max exceeds it by more than 2^8
-// (then O and the sum are rescaled); the stale max is exact because O and
-// the sum share it.
+// The running max is an integer in log2 units, raised only when needed: a
+// unit's probabilities are formed against the current max, and only when
+// some lane's sum over the unit exceeds 2^8 (which any logit more than 8
+// above the max causes) is the true row max taken, O and the sum rescaled and
+// the unit redone. Row sums are taken over the bf16-rounded probabilities
+// that enter the PV product, so numerator and denominator use the same
+// weights.
 //
 // Workgroups are renumbered so that each of the eight XCDs (which receive
 // workgroup ids round-robin) walks a contiguous run of query tiles of the
-// same head: neighbouring query tiles keep overlapping key tiles, which then
-// hit in that XCD's L2.
+// same head.
 #include <cstdlib>
 
 #include "device_common.h"
@@ -36,12 +43,17 @@
 namespace vsa {
 namespace {
 
-constexpr int kSplits = 4;
-constexpr int kThreads = 64 * kSplits;
+constexpr int kSplits = 4;                   // key splits per query tile
+constexpr int kWaves = 2 * kSplits;          // two query halves per split
+constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -1.0e30f;
-constexpr float kRescaleSlack = 8.0f;
+constexpr float kSumLimit = 256.0f;
+
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -64,34 +76,65 @@ __device__ inline void work_item(const Plan &p, int total, int &b, int &h, int &
   tq = rem2;
 }
 
+// True when every slot of `tile` holds a real token (wave-uniform inputs,
+// so this compiles to scalar code).
+__device__ inline bool tile_full(const Plan &p, int s, int tile) {
+  if (tile < p.n_prefix_tiles) {
+    int seg = 0;
+    while (seg + 1 < p.n_prefix && tile >= p.prefix_tile0[seg + 1]) ++seg;
+    return (tile - p.prefix_tile0[seg] + 1) * kTile <= p.prefix_len[seg];
+  }
+  if (p.video_full[s]) return true;
+  const int v = tile - p.n_prefix_tiles;
+  const int gw = p.grid_w[s], gh = p.grid_h[s];
+  const int wi = v % gw, hi = (v / gw) % gh, ti = v / (gw * gh);
+  return (ti + 1) * p.shape[s][0] <= p.T && (hi + 1) * p.shape[s][1] <= p.Hv &&
+         (wi + 1) * p.shape[s][2] <= p.Wv;
+}
+
+// Both waves' copies have landed and both waves are done reading the slot
+// they just used: own copies drained (vector-memory counter), then the
+// workgroup barrier.
+__device__ inline void sync_slots() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+}
+
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bf16_kernel(Plan p, int total, const bf16_bits *__restrict__ qt,
                       const bf16_bits *__restrict__ kt, const bf16_bits *__restrict__ vt,
                       const int32_t *__restrict__ s2t, const int32_t *__restrict__ kv_idx,
                       float scale_log2, bf16_bits *__restrict__ out,
                       float *__restrict__ lse) {
-  constexpr int NC = D / 16, NDB = D / 32, LDO = D + 1;
-  __shared__ float sm_m[kSplits][kTile], sm_l[kSplits][kTile];
-  __shared__ float osum[kTile * LDO];
+  constexpr int NC = D / 16, NDB = D / 32;
+  constexpr int UNIT = 32 * D;                 // elements of one unit's K (or V)
+  // Two slots, each K then V of one unit. Distinct objects: a slot is only
+  // read while the other one is being filled.
+  __shared__ __attribute__((aligned(1024))) bf16_bits ring0_all[kSplits * 2 * UNIT];
+  __shared__ __attribute__((aligned(1024))) bf16_bits ring1_all[kSplits * 2 * UNIT];
 
   int b, h, tq;
   work_item(p, total, b, h, tq);
   const int s = h % p.n_shapes;
   const int bh = b * p.H + h;
-  const int ks = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int qb = wave % 2, ks = wave / 2;
+  bf16_bits *const ring0 = ring0_all + ks * 2 * UNIT;
+  bf16_bits *const ring1 = ring1_all + ks * 2 * UNIT;
   const int lane = threadIdx.x % 64;
   const int g = lane / 32, l32 = lane % 32;
   const int npt = p.n_prefix_tiles;
   const bool full_row = p.dense || tq < npt;
   const int n_kv = full_row ? p.n_tiles[s] : npt + p.k[s];
+  // The kept-tile list is read through the constant address space (scalar
+  // loads), which keeps it off the vector-memory counter of the copies.
   typedef const __attribute__((address_space(4))) int32_t *const_i32_ptr;
   const const_i32_ptr kv_row =
       full_row ? nullptr
                : (const_i32_ptr)(kv_idx + ((int64_t)bh * p.max_vt + (tq - npt)) * p.k_max);
   const int64_t head_base = (int64_t)bh * p.max_tiles;
   const int32_t *map = s2t + (int64_t)s * p.max_tiles * kTile;
-  const int n_mine = n_kv > ks ? (n_kv - ks + kSplits - 1) / kSplits : 0;
 
   constexpr int TB = kTile * D * 2;
   const uint32_t head_bytes = (uint32_t)p.max_tiles * TB;
@@ -100,198 +143,197 @@ void attn_bf16_kernel(Plan p, int total, const bf16_bits *__restrict__ qt,
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vt + head_base * (kTile * D), head_bytes);
   const int voff = lane * 16;
 
-bf16x8 qf[2][NC];           // Q^T fragments (B operand of S^T = K Q^T)
+  bf16x8 qf[NC];              // this wave's Q^T fragments (B operand of S^T = K Q^T)
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int cc = 0; cc < NC; ++cc) qf[cc] = buffer_load16(rq, voff, tq * TB + (qb * NC + cc) * 1024);
+  f32x16 o[NDB];
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc)
-      qf[qb][cc] = buffer_load16(rq, voff, tq * TB + (qb * NC + cc) * 1024);
-  bf16x8 kbuf[2][NC], vbuf[2][NDB][2];
-  f32x16 sbuf[2][2];          // [unit parity][qb]
-  f32x16 o[2][NDB];
-  float m_use[2] = {kNegBig, kNegBig}, l_run[2] = {0.f, 0.f};
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[qb][db][r] = 0.f;
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+  float m_use = kNegBig, l_run = 0.f;
 
+  // Global tile of the i-th key tile of the row; ok = false for an index
+  // outside the head's video tiles (then the tile is fully masked).
+  const int n_mine = n_kv > ks ? (n_kv - ks + kSplits - 1) / kSplits : 0;
   auto tile_of = [&](int i, bool &ok) -> int {
-    const int e = ks + kSplits * i;
     ok = true;
-    if (full_row || e < npt) return e;
-    const int j = kv_row[e - npt];
+    i = ks + kSplits * i;
+    if (full_row || i < npt) return i;
+    const int j = kv_row[i - npt];
     if ((unsigned)j >= (unsigned)p.n_vt[s]) {
       ok = false;
       return 0;
     }
     return npt + j;
   };
+  // Real-key mask of a tile (bit = slot), ~0 for a full tile.
   auto tile_mask = [&](int tile, bool ok) -> uint64_t {
-    const uint64_t m = __ballot(slot_token(p, s, tile, lane) >= 0);
-    return ok ? m : 0ull;
+    if (!ok) return 0ull;
+    if (tile_full(p, s, tile)) return ~0ull;
+    return __ballot(slot_token(p, s, tile, lane) >= 0);
   };
-  auto load_k = [&](int buf, int tile, int kb) {
+  // Copy of unit (tile, key half kb) into a slot: wave 0 the K blocks, wave 1
+  // the V blocks.
+  auto issue = [&](bf16_bits *slot, int tile, int kb) {
+    if (qb == 0) {
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc)
-      kbuf[buf][cc] = buffer_load16(rk, voff, tile * TB + (kb * NC + cc) * 1024);
-  };
-  auto load_v = [&](int buf, int tile, int kb) {
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-        vbuf[buf][db][jj] = buffer_load16(rv, voff, tile * TB + (db * 4 + 2 * kb + jj) * 1024);
-  };
-  auto qk = [&](int buf, f32x16 (&acc)[2]) {
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[qb][r] = 0.f;
-#pragma unroll
-      for (int cc = 0; cc < NC; ++cc) acc[qb] = mfma32(kbuf[buf][cc], qf[qb][cc], acc[qb]);
-    }
-  };
-  auto apply_mask = [&](f32x16 (&sc)[2], uint32_t mask32) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int k0 = (r / 4) * 8 + (r % 4);
-      const bool keep = g ? ((mask32 >> (k0 + 4)) & 1u) : ((mask32 >> k0) & 1u);
-      sc[0][r] = keep ? sc[0][r] : -INFINITY;
-      sc[1][r] = keep ? sc[1][r] : -INFINITY;
-    }
-  };
-  auto exp_unit = [&](const f32x16 &sc, float mref, bf16x8 (&pf)[2], float &psum, float &mx) {
-    float m4[4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-      m4[a] = fmaxf(fmaxf(sc[4 * a], sc[4 * a + 1]), fmaxf(sc[4 * a + 2], sc[4 * a + 3]));
-    mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                     false, false);
-    mx = fmaxf(fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])), mx) * scale_log2;
-    float pv[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], scale_log2, -mref));
-    float s8[8];
-#pragma unroll
-    for (int a = 0; a < 8; ++a) s8[a] = pv[2 * a] + pv[2 * a + 1];
-    psum = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
-#pragma unroll
-    for (int r = 0; r < 16; ++r) pf[r / 8][r % 8] = (__bf16)pv[r];
-  };
-  // Softmax of one unit (S^T in sc) and its PV product with V buffer vb.
-  auto step = [&](f32x16 (&sc)[2], int vb) {
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      bf16x8 pf[2];
-      float psum, mx;
-      exp_unit(sc[qb], m_use[qb], pf, psum, mx);
-      if (__any(mx > m_use[qb] + kRescaleSlack)) {
-        const float m_new = ceilf(fmaxf(m_use[qb], mx));
-        const float alpha = __builtin_amdgcn_exp2f(m_use[qb] - m_new);
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
-        m_use[qb] = m_new;
-        float unused;
-        exp_unit(sc[qb], m_new, pf, psum, unused);
-      }
-      l_run[qb] += psum;
+      for (int cc = 0; cc < NC; ++cc)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(slot + cc * 512), 16, voff,
+                                                 tile * TB + (kb * NC + cc) * 1024, 0, 0);
+    } else {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) o[qb][db] = mfma32(vbuf[vb][db][jj], pf[jj], o[qb][db]);
+        for (int jj = 0; jj < 2; ++jj)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rv, (lds_ptr_t)(slot + UNIT + (db * 2 + jj) * 512), 16, voff,
+              tile * TB + (db * 4 + 2 * kb + jj) * 1024, 0, 0);
+    }
+  };
+  auto frag = [&](const bf16_bits *slot, int blk) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8 *>(slot + blk * 512 + lane * 8);
+  };
+  // P^T of a unit (bf16) against the running max, and the lane's sum of the
+  // rounded probabilities.
+  auto probs = [&](const f32x16 &sc, bf16x8 (&pf)[2]) -> float {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        pf[j][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[8 * j + e], scale_log2, -m_use));
+      const bf16x8 v = pf[j];
+      a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), ones, a0, false);
+      a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), ones, a1, false);
+      a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), ones, a0, false);
+      a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), ones, a1, false);
+    }
+    return a0 + a1;
+  };
+  // One unit from a slot: S^T, the mask of a partly filled tile, softmax
+  // (with the rare raise of the max), PV.
+  auto unit = [&](const bf16_bits *slot, uint32_t mask32) {
+    bf16x8 kf[NC];
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) kf[cc] = frag(slot, cc);
+    f32x16 sc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) sc = mfma32(kf[cc], qf[cc], sc);
+    if (mask32 != 0xFFFFFFFFu) {
+      // Element r of lane (g, l32) is key (r/4)*8 + g*4 + r%4 of the unit.
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int k0i = (r / 4) * 8 + g * 4 + (r % 4);
+        sc[r] = ((mask32 >> k0i) & 1u) ? sc[r] : -INFINITY;
+      }
+    }
+    bf16x8 pf[2];
+    float ps = probs(sc, pf);
+    if (__builtin_expect(__any(ps > kSumLimit), 0)) {
+      // A logit exceeded the running max by more than the slack: take the
+      // unit's true row max (both lane halves), move the max there, redo.
+      float m = sc[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) m = fmaxf(m, sc[r]);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m),
+                                                       false, false);
+      m = fmaxf(fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])), m) * scale_log2;
+      const float m_new = fmaxf(ceilf(fmaxf(m_use, m)), kNegBig);
+      const float alpha = __builtin_amdgcn_exp2f(m_use - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      m_use = m_new;
+      ps = probs(sc, pf);
+    }
+    l_run += ps;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const bf16x8 va = frag(slot + UNIT, db * 2), vb = frag(slot + UNIT, db * 2 + 1);
+      o[db] = mfma32(va, pf[0], o[db]);
+      o[db] = mfma32(vb, pf[1], o[db]);
     }
   };
 
+  // Unit 2i + kb is key half kb of the row's i-th tile; even units use slot
+  // ring0, odd units ring1. The copy of the next unit is issued before the
+  // current one is computed.
+  // Every wave runs the same number of steps (barriers); a split with fewer
+  // tiles idles through the last step.
+  const int n_steps = (n_kv + kSplits - 1) / kSplits;
+  bool ok = false;
+  int t = 0;
+  uint64_t mask = 0;
   if (n_mine > 0) {
-    // Unit u = 2i + kb: key half kb of the wave's i-th tile, K in kbuf[u%2]
-    // and V in vbuf[u%2], both fetched two units ahead.
-    bool ok0, ok1 = false;
-    int t0 = tile_of(0, ok0), t1 = 0;
-    if (n_mine > 1) t1 = tile_of(1, ok1);
-    uint64_t mask0 = tile_mask(t0, ok0), mask1 = 0;
-    load_k(0, t0, 0);
-    load_v(0, t0, 0);
-    load_k(1, t0, 1);
-    load_v(1, t0, 1);
-    qk(0, sbuf[0]);
-    if (n_mine > 1) load_k(0, t1, 0);
-    for (int i = 0; i < n_mine; ++i) {
-      const bool more = i + 1 < n_mine;
-      if (more) mask1 = tile_mask(t1, ok1);
-      // unit 2i
-      qk(1, sbuf[1]);                                 // S of unit 2i+1
-      if (more) load_k(1, t1, 1);                     // K of unit 2i+3
-      if ((uint32_t)mask0 != 0xFFFFFFFFu) apply_mask(sbuf[0], (uint32_t)mask0);
-      step(sbuf[0], 0);
-      if (more) load_v(0, t1, 0);                     // V of unit 2i+2
-      // unit 2i+1
-      if (more) qk(0, sbuf[0]);                       // S of unit 2i+2
-      bool ok2 = false;
-      int t2 = 0;
-      if (i + 2 < n_mine) {
-        t2 = tile_of(i + 2, ok2);
-        load_k(0, t2, 0);                             // K of unit 2i+4
-      }
-      if ((uint32_t)(mask0 >> 32) != 0xFFFFFFFFu) apply_mask(sbuf[1], (uint32_t)(mask0 >> 32));
-      step(sbuf[1], 1);
-      if (more) load_v(1, t1, 1);                     // V of unit 2i+3
-      t0 = t1;
-      mask0 = mask1;
-      t1 = t2;
-      ok1 = ok2;
+    t = tile_of(0, ok);
+    mask = tile_mask(t, ok);
+    issue(ring0, t, 0);
+  }
+  sync_slots();
+  for (int i = 0; i < n_steps; ++i) {
+    const bool mine = i < n_mine;
+    if (mine) {
+      issue(ring1, t, 1);
+      unit(ring0, (uint32_t)mask);
     }
+    sync_slots();
+    const bool more = i + 1 < n_mine;
+    bool ok1 = false;
+    int t1 = 0;
+    if (more) {
+      t1 = tile_of(i + 1, ok1);
+      issue(ring0, t1, 0);
+    }
+    if (mine) unit(ring1, (uint32_t)(mask >> 32));
+    sync_slots();
+    t = t1;
+    mask = more ? tile_mask(t1, ok1) : 0ull;
   }
 
-  // Merge the four key splits.
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32);
+  // Merge the four key splits of each query half (the rings are free now:
+  // the last step ended with a barrier).
+  float *osum = reinterpret_cast<float *>(ring0_all);       // [64][D], swizzled
+  float *sm_m = reinterpret_cast<float *>(ring1_all);       // [kSplits][64]
+  float *sm_l = sm_m + kSplits * kTile;
+  const int q = qb * 32 + l32;
+  {
+    const float lt = l_run + __shfl_xor(l_run, 32);
     if (g == 0) {
-      sm_m[ks][qb * 32 + l32] = m_use[qb];
-      sm_l[ks][qb * 32 + l32] = lt;
+      sm_m[ks * kTile + q] = m_use;
+      sm_l[ks * kTile + q] = lt;
     }
   }
   __syncthreads();
+  float M = sm_m[q];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int q = qb * 32 + l32;
-    float M = sm_m[0][q];
+  for (int w = 1; w < kSplits; ++w) M = fmaxf(M, sm_m[w * kTile + q]);
+  float L = 0.f;
 #pragma unroll
-    for (int w = 1; w < kSplits; ++w) M = fmaxf(M, sm_m[w][q]);
-    float L = 0.f;
-#pragma unroll
-    for (int w = 0; w < kSplits; ++w) L += sm_l[w][q] * __builtin_amdgcn_exp2f(sm_m[w][q] - M);
-    const float f = __builtin_amdgcn_exp2f(m_use[qb] - M) / L;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[qb][db][r] *= f;
-  }
+  for (int w = 0; w < kSplits; ++w) L += sm_l[w * kTile + q] * __builtin_amdgcn_exp2f(sm_m[w * kTile + q] - M);
+  const float f = __builtin_amdgcn_exp2f(m_use - M) / L;
+  // Element (q, c) of the merged tile sits at q*D + (c ^ (q % 32)).
   for (int turn = 0; turn < kSplits; ++turn) {
     if (ks == turn) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int q = qb * 32 + l32;
-            const int c = db * 32 + (r / 4) * 8 + g * 4 + (r % 4);
-            if (turn == 0)
-              osum[q * LDO + c] = o[qb][db][r];
-            else
-              osum[q * LDO + c] += o[qb][db][r];
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int c = db * 32 + (r / 4) * 8 + g * 4 + (r % 4);
+          float &dst = osum[q * D + (c ^ l32)];
+          if (turn == 0)
+            dst = o[db][r] * f;
+          else
+            dst += o[db][r] * f;
+        }
     }
     __syncthreads();
   }
-
   const int32_t *qmap = map + (int64_t)tq * kTile;
   bf16_bits *out_bh = out + (int64_t)bh * p.N * D;
   for (int idx = threadIdx.x; idx < kTile * D / 8; idx += blockDim.x) {
@@ -300,18 +342,18 @@ bf16x8 qf[2][NC];           // Q^T fragments (B operand of S^T = K Q^T)
     if (tok < 0) continue;
     bf16x8 v8;
 #pragma unroll
-    for (int e8 = 0; e8 < 8; ++e8) v8[e8] = (__bf16)osum[row * LDO + ch * 8 + e8];
+    for (int e8 = 0; e8 < 8; ++e8) v8[e8] = (__bf16)osum[row * D + ((ch * 8 + e8) ^ (row % 32))];
     *reinterpret_cast<bf16x8 *>(out_bh + (int64_t)tok * D + ch * 8) = v8;
   }
   if (lse && threadIdx.x < kTile) {
-    const int q = threadIdx.x;
-    const int32_t tok = qmap[q];
+    const int qq = threadIdx.x;
+    const int32_t tok = qmap[qq];
     if (tok >= 0) {
-      float M = sm_m[0][q];
-      for (int w = 1; w < kSplits; ++w) M = fmaxf(M, sm_m[w][q]);
-      float L = 0.f;
-      for (int w = 0; w < kSplits; ++w) L += sm_l[w][q] * __builtin_amdgcn_exp2f(sm_m[w][q] - M);
-      lse[(int64_t)bh * p.N + tok] = M * kLn2 + logf(L);
+      float MM = sm_m[qq];
+      for (int w = 1; w < kSplits; ++w) MM = fmaxf(MM, sm_m[w * kTile + qq]);
+      float LL = 0.f;
+      for (int w = 0; w < kSplits; ++w) LL += sm_l[w * kTile + qq] * __builtin_amdgcn_exp2f(sm_m[w * kTile + qq] - MM);
+      lse[(int64_t)bh * p.N + tok] = MM * kLn2 + logf(LL);
     }
   }
 }

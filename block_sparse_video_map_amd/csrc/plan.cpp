@@ -64,6 +64,7 @@ int make_plan_geometry(const vsa_problem *prob, Plan *p) {
     int64_t nvt = gt * gh * gw;
     if (nvt > VSA_MAX_VIDEO_TILES) return VSA_ERR_SIZE;
     p->grid_t[s] = (int32_t)gt; p->grid_h[s] = (int32_t)gh; p->grid_w[s] = (int32_t)gw;
+    p->video_full[s] = prob->T % pt == 0 && prob->Hv % ph == 0 && prob->Wv % pw == 0;
     p->n_vt[s] = (int32_t)nvt;
     p->n_tiles[s] = (int32_t)(nvt + p->n_prefix_tiles);
     if (p->n_tiles[s] > p->max_tiles) p->max_tiles = p->n_tiles[s];

@@ -17,6 +17,7 @@ struct Plan {
   int32_t n_shapes;
   int32_t shape[VSA_MAX_SHAPES][3];            // (pt, ph, pw)
   int32_t grid_t[VSA_MAX_SHAPES], grid_h[VSA_MAX_SHAPES], grid_w[VSA_MAX_SHAPES];
+  int32_t video_full[VSA_MAX_SHAPES];          // every video tile of the shape is full
   int32_t n_prefix_tiles;
   int32_t n_tiles[VSA_MAX_SHAPES];
   int32_t n_vt[VSA_MAX_SHAPES];

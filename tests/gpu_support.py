@@ -192,6 +192,11 @@ def bf16_stats(got: np.ndarray, want: np.ndarray):
 
 BF16_MAX_ABS, BF16_MEAN_ABS = 2e-2, 5e-3
 F32_MAX_ABS = 1e-5
+# bf16 path: the row sum behind the LSE is taken over the bf16-rounded
+# probabilities that weight V (each within 2^-9 relative of the exact one), so
+# the log of the sum is within 2^-9 of the exact LSE, plus fp32 rounding of the
+# logits and the sum.
+BF16_LSE_ABS = 2.0 ** -9 + 1e-4
 
 
 def default_scale(d):
