@@ -1,10 +1,12 @@
 // Step 2: pooled tile descriptors (double) and their dot products (float).
 //
-// Pooling runs one workgroup per (video tile, batch*head, Q|K): the tile is
-// read once from the tiled layout into LDS, reduced over its real slots in
-// double, and projected (mean gate) or projected-then-reduced (TripPool).
+// Mean gate: one workgroup per 16 video tiles of one (batch*head, Q|K); the
+// means are reduced in double and multiplied by the head's gate on the f64
+// MFMA. TripPool: one workgroup per (video tile, batch*head, Q|K); the tile's
+// tokens are projected on the f64 MFMA, then reduced to [Avg | Max | Min].
 // Scoring is a double-precision GEMM per head on the f64 MFMA, 64x64 outputs
-// per workgroup, rounded once to float on the way out.
+// per workgroup with operands staged through LDS, rounded once to float on
+// the way out.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -23,52 +25,126 @@ __device__ inline void load_tile_f32(const T *__restrict__ src, float *xs) {
 }
 
 // VSA: desc = mean over real slots, times the head's gate.
+//
+// One workgroup takes 16 video tiles of one (batch*head, Q|K). Means: every
+// thread loads four 16-byte vectors of a tile (two slots x 8 channels of two
+// channel groups), adds the two slots in double, and the 32 slot pairs of a
+// channel are then summed from LDS; pad slots hold zero in the tiled copy, so
+// the sum over all 64 slots divided by the real-slot count is the mean.
+// Gate: the 16 x D means times the D x D gate on the 16x16x4 f64 MFMA, wave w
+// owning 16-column blocks w, w+4.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+constexpr int kPoolTiles = 16;
+
+template <typename T>
+__device__ inline void load8_f32(const T *__restrict__ src, float (&v)[8]);
+template <>
+__device__ inline void load8_f32<bf16_bits>(const bf16_bits *__restrict__ src, float (&v)[8]) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 w = *reinterpret_cast<const u32x4 *>(src);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+template <>
+__device__ inline void load8_f32<float>(const float *__restrict__ src, float (&v)[8]) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(src);
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(src + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = a[i];
+    v[4 + i] = b[i];
+  }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void pool_mean_gate_kernel(
     Plan p, const T *__restrict__ qt, const T *__restrict__ kt,
     const int32_t *__restrict__ s2t, const float *__restrict__ wq,
     const float *__restrict__ wk, double *__restrict__ pooled) {
-  constexpr int LD = D + 1;
-  __shared__ float xs[kTile * LD];
-  __shared__ double mean[D];
-  __shared__ int valid[kTile];
+  constexpr int NV = kTile * D / 8;          // 8-element vectors per tile
+  constexpr int VPT = NV / 256;              // vectors per thread (4 for D=128)
+  static_assert(VPT >= 1 && NV % 256 == 0, "tile must split evenly over 256 threads");
+  __shared__ double part[32 * D];            // [slot pair][channel]
+  constexpr int LM = D + 1;                  // padded rows: conflict-free MFMA reads
+  __shared__ double mean[kPoolTiles * LM];   // [tile][channel]
+  __shared__ int count[kPoolTiles];
 
-  const int vt_i = blockIdx.x, bh = blockIdx.y, which = blockIdx.z;
+  const int bh = blockIdx.y, which = blockIdx.z;
   const int h = bh % p.H, s = h % p.n_shapes;
-  if (vt_i >= p.n_vt[s]) return;
-  const int tile = p.n_prefix_tiles + vt_i;
-  const T *src = (which == 0 ? qt : kt) + ((int64_t)bh * p.max_tiles + tile) * (kTile * D);
+  const int n = p.n_vt[s];
+  const int vt0 = blockIdx.x * kPoolTiles;
+  if (vt0 >= n) return;
+  const int nt = min(kPoolTiles, n - vt0);
+  const T *src = (which == 0 ? qt : kt) + ((int64_t)bh * p.max_tiles + p.n_prefix_tiles + vt0) *
+                                              (kTile * D);
   const float *w = (which == 0 || !wk ? wq : wk) + (int64_t)h * D * D;
+  const int t = threadIdx.x, lane = t % 64, wave = t / 64;
 
-  if (threadIdx.x < kTile)
-    valid[threadIdx.x] = s2t[((int64_t)s * p.max_tiles + tile) * kTile + threadIdx.x] >= 0;
-  load_tile_f32<T, D, LD>(src, xs);
-  __syncthreads();
-
-  // Four independent partial sums per channel / output keep the double adds
-  // and FMAs from forming one long dependency chain.
-  if (threadIdx.x < D) {
-    const int c = threadIdx.x;
-    double part[4] = {0.0, 0.0, 0.0, 0.0};
-    int n = 0;
-#pragma unroll 4
-    for (int sl = 0; sl < kTile; ++sl) {
-      if (valid[sl]) {
-        part[sl % 4] += (double)xs[sl * LD + c];
-        ++n;
-      }
-    }
-    mean[c] = ((part[0] + part[1]) + (part[2] + part[3])) / (double)n;
+  // Real-slot counts: wave w counts tiles w, w+4, ... (one slot per lane).
+  for (int tt = wave; tt < nt; tt += 4) {
+    const int tok = s2t[((int64_t)s * p.max_tiles + p.n_prefix_tiles + vt0 + tt) * kTile + lane];
+    const int c = __popcll(__ballot(tok >= 0));
+    if (lane == 0) count[tt] = c;
   }
+  for (int tt = 0; tt < nt; ++tt) {
+    const T *tile = src + (int64_t)tt * kTile * D;
+    // Vector v of the tile (row layout): slot (v/64/(D/16))*32 + v%32,
+    // channels ((v/64)%(D/16))*16 + ((v%64)/32)*8 + 0..7.
+    double acc[VPT / 2][8];
+#pragma unroll
+    for (int a = 0; a < VPT / 2; ++a)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[a][e] = 0.0;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      float v[8];
+      load8_f32<T>(tile + (int64_t)(t + 256 * i) * 8, v);
+      // i and i + VPT/2 hold the two slot halves of the same channels.
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[i % (VPT / 2)][e] += (double)v[e];
+    }
+#pragma unroll
+    for (int a = 0; a < VPT / 2; ++a) {
+      const int vec = t + 256 * a;
+      const int blk = vec / 64;
+      const int c0 = (blk % (D / 16)) * 16 + ((vec % 64) / 32) * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[(lane % 32) * D + c0 + e] = acc[a][e];
+    }
+    __syncthreads();
+    if (t < D) {
+      double sum = 0.0;
+#pragma unroll 8
+      for (int r = 0; r < 32; ++r) sum += part[r * D + t];
+      mean[tt * LM + t] = sum / (double)count[tt];
+    }
+    __syncthreads();
+  }
+  for (int tt = nt; tt < kPoolTiles; ++tt)
+    if (t < D) mean[tt * LM + t] = 0.0;        // rows past the last tile
   __syncthreads();
 
-  if (threadIdx.x < D) {
-    const int j = threadIdx.x;
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll 4
-    for (int c = 0; c < D; ++c) acc[c % 4] = fma(mean[c], (double)w[c * D + j], acc[c % 4]);
-    pooled[(((int64_t)which * p.B * p.H + bh) * p.max_vt + vt_i) * D + j] =
-        (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  // Gate product on the f64 MFMA. A: lane l holds mean[l%16][k0 + l/16];
+  // B: gate[k0 + l/16][col0 + l%16]; D element e: row 4e + l/16, column l%16.
+  const int l16 = lane % 16, g4 = lane / 16;
+  double *dst = pooled + (((int64_t)which * p.B * p.H + bh) * p.max_vt + vt0) * D;
+  for (int cb = wave; cb < D / 16; cb += 4) {
+    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 8
+    for (int k0 = 0; k0 < D; k0 += 4) {
+      const double a = mean[l16 * LM + k0 + g4];
+      const double b = (double)w[(k0 + g4) * D + cb * 16 + l16];
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 4 * e + g4;
+      if (row < nt) dst[(int64_t)row * D + cb * 16 + l16] = acc[e];
+    }
   }
 }
 
@@ -79,8 +155,6 @@ __global__ __launch_bounds__(256) void pool_mean_gate_kernel(
 // its column of P (transposed in LDS), MFMA m contracting channel m of that
 // group. Each lane then holds four tokens (rows 4e + l/16) of one column
 // (l % 16); the statistics are reduced across lanes, then across waves.
-typedef double f64x4 __attribute__((ext_vector_type(4)));
-
 template <typename T, int D, int R>
 __global__ __launch_bounds__(256) void pool_trippool_kernel(
     Plan p, const T *__restrict__ qt, const T *__restrict__ kt,
@@ -184,67 +258,82 @@ __global__ __launch_bounds__(256) void pool_trippool_kernel(
 // doubles of its row at offset 4*(l/16): MFMA m then contracts channel
 // k0 + 4*(l/16) + m of both operands, so the four products cover the slice.
 constexpr int kSB = 64;   // output block edge
+constexpr int kKC = 16;   // contraction chunk staged in LDS
+constexpr int kLK = kKC + 2;   // padded LDS row (doubles)
 
+// Scores: S = Qd Kd^T per (batch, head), 64x64 outputs per workgroup of four
+// waves (each 32x32 = 2x2 blocks of the 16x16x4 f64 MFMA). The 64-row slices
+// of Qd and Kd are staged through LDS in chunks of 16 contraction columns,
+// double-buffered: every thread fetches 4 doubles of each for the next chunk
+// while the current chunk is multiplied.
 __global__ __launch_bounds__(256) void scores_kernel(Plan p, int r,
                                                      const double *__restrict__ pooled,
                                                      float *__restrict__ scores) {
+  __shared__ double As[2][kSB * kLK];
+  __shared__ double Bs[2][kSB * kLK];
   const int bh = blockIdx.z, h = bh % p.H, s = h % p.n_shapes;
   const int n = p.n_vt[s];
   const int i0 = blockIdx.y * kSB, j0 = blockIdx.x * kSB;
   if (i0 >= n || j0 >= n) return;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
-  const int lane = threadIdx.x % 64, g = lane / 16, l16 = lane % 16;
-  const int wi = i0 + (wave / 2) * 32, wj = j0 + (wave % 2) * 32;
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t / 64);
+  const int lane = t % 64, g = lane / 16, l16 = lane % 16;
+  const int wr = (wave / 2) * 32, wc = (wave % 2) * 32;    // wave's block inside the 64x64
   const double *Qd = pooled + (int64_t)bh * p.max_vt * r;
   const double *Kd = pooled + ((int64_t)p.B * p.H + bh) * p.max_vt * r;
 
-  int ra[2], rb[2];
-  bool va[2], vb[2];
+  // Thread t stages row t/4, columns 4*(t%4) .. +3 of the chunk, for A and B.
+  const int srow = t / 4, scol = (t % 4) * 4;
+  const bool oka = i0 + srow < n, okb = j0 + srow < n;
+  const double *qa = Qd + (int64_t)(i0 + srow) * r + scol;
+  const double *kb = Kd + (int64_t)(j0 + srow) * r + scol;
+  double ra[4], rb[4];
+  auto fetch = [&](int k0) {
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    ra[a] = wi + a * 16 + l16;
-    rb[a] = wj + a * 16 + l16;
-    va[a] = ra[a] < n;
-    vb[a] = rb[a] < n;
-  }
+    for (int m = 0; m < 4; ++m) {
+      const bool okk = k0 + scol + m < r;
+      ra[m] = (oka && okk) ? qa[k0 + m] : 0.0;
+      rb[m] = (okb && okk) ? kb[k0 + m] : 0.0;
+    }
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      As[buf][srow * kLK + scol + m] = ra[m];
+      Bs[buf][srow * kLK + scol + m] = rb[m];
+    }
+  };
+
   f64x4 acc[2][2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = (f64x4){0.0, 0.0, 0.0, 0.0};
 
-  // Operands of one 16-wide slice: av/bv[buffer][block][m]; the next slice is
-  // fetched while the current one is multiplied.
-  double av[2][2][4], bv[2][2][4];
-  auto fetch = [&](int buf, int k0) {
-    const int kk = k0 + 4 * g;          // r is a multiple of 4: groups are all-in or all-out
+  const int nchunks = (r + kKC - 1) / kKC;
+  fetch(0);
+  stage(0);
+  __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nchunks) fetch((c + 1) * kKC);
+    // A: lane l holds row l%16 (of a 16-row block), column k + l/16; B alike.
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const bool oka = va[a] && kk < r, okb = vb[a] && kk < r;
+    for (int k = 0; k < kKC; k += 4) {
+      double av[2], bv[2];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        av[buf][a][m] = oka ? Qd[(int64_t)ra[a] * r + kk + m] : 0.0;
-        bv[buf][a][m] = okb ? Kd[(int64_t)rb[a] * r + kk + m] : 0.0;
+      for (int a = 0; a < 2; ++a) {
+        av[a] = As[buf][(wr + a * 16 + l16) * kLK + k + g];
+        bv[a] = Bs[buf][(wc + a * 16 + l16) * kLK + k + g];
       }
-    }
-  };
-  auto multiply = [&](int buf) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[buf][a][m], bv[buf][b][m],
-                                                           acc[a][b], 0, 0, 0);
-  };
-  fetch(0, 0);
-  for (int k0 = 0; k0 < r; k0 += 32) {
-    if (k0 + 16 < r) fetch(1, k0 + 16);
-    multiply(0);
-    if (k0 + 16 >= r) break;
-    if (k0 + 32 < r) fetch(0, k0 + 32);
-    multiply(1);
+          acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[b], acc[a][b], 0, 0, 0);
+    }
+    if (c + 1 < nchunks) stage(buf ^ 1);
+    __syncthreads();
   }
   // D element e of lane l is row 4*e + l/16, column l % 16 of the block.
   float *out = scores + (int64_t)bh * p.max_vt * p.max_vt;
@@ -254,7 +343,7 @@ __global__ __launch_bounds__(256) void scores_kernel(Plan p, int r,
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = wi + a * 16 + 4 * e + g, j = wj + b * 16 + l16;
+        const int i = i0 + wr + a * 16 + 4 * e + g, j = j0 + wc + b * 16 + l16;
         if (i < n && j < n) out[(int64_t)i * p.max_vt + j] = (float)acc[a][b][e];
       }
 }
@@ -265,7 +354,8 @@ hipError_t pool_t(const Plan &p, int mode, int R, const void *qt, const void *kt
                   hipStream_t st) {
   dim3 grid(p.max_vt, p.B * p.H, 2);
   if (mode == VSA_SCORE_MEAN_GATE) {
-    hipLaunchKernelGGL((pool_mean_gate_kernel<T, D>), grid, dim3(256), 0, st, p,
+    dim3 grid_mg((p.max_vt + kPoolTiles - 1) / kPoolTiles, p.B * p.H, 2);
+    hipLaunchKernelGGL((pool_mean_gate_kernel<T, D>), grid_mg, dim3(256), 0, st, p,
                        (const T *)qt, (const T *)kt, s2t, wq, wk, pooled);
   } else {
     switch (R) {
