@@ -130,26 +130,31 @@ def gather(x: np.ndarray, tmap: TileMap) -> np.ndarray:
 # 3. Pool
 # --------------------------------------------------------------------------
 
-def _video_part(xt: np.ndarray, tmap: TileMap):
-    v = tmap.valid()[tmap.n_prefix_tiles:]
-    return np.asarray(xt[tmap.n_prefix_tiles:], dtype=np.float64), v
+def _tiles_part(xt: np.ndarray, tmap: TileMap, tiles=None):
+    """Rows and real-slot masks of the given tiles (default: the video tiles)."""
+    if tiles is None:
+        tiles = np.arange(tmap.n_prefix_tiles, tmap.n_tiles)
+    tiles = np.asarray(tiles, dtype=np.int64)
+    return np.asarray(xt[tiles], dtype=np.float64), tmap.valid()[tiles]
 
 
-def pool_mean_gate(xt: np.ndarray, tmap: TileMap, gate: np.ndarray) -> np.ndarray:
+def pool_mean_gate(xt: np.ndarray, tmap: TileMap, gate: np.ndarray, tiles=None) -> np.ndarray:
     """VSA tile descriptor: mean of a video tile's real rows, times the gate.
 
     The gating projection to_gate_compress decides which tiles a query tile
     attends to ("From 650 s to 72 s", section "The method"). Reading: the
     same per-head d x d gate multiplies the pooled Q tile and the pooled K
-    tile; pad slots are left out of the mean. Returns float64 [n_video, r].
+    tile; pad slots are left out of the mean. ``tiles`` picks other tiles
+    (the reference stream of the two-stream budget). Returns float64
+    [n_tiles, r].
     """
-    x, v = _video_part(xt, tmap)
+    x, v = _tiles_part(xt, tmap, tiles)
     counts = v.sum(axis=1).astype(np.float64)
     mean = (x * v[:, :, None]).sum(axis=1) / counts[:, None]
     return mean @ np.asarray(gate, dtype=np.float64)
 
 
-def pool_trippool(xt: np.ndarray, tmap: TileMap, proj: np.ndarray) -> np.ndarray:
+def pool_trippool(xt: np.ndarray, tmap: TileMap, proj: np.ndarray, tiles=None) -> np.ndarray:
     """Veda TripPool tile descriptor: [Avg, Max, Min] of projected tokens.
 
     Each real token of a video tile is projected by the head's d x r matrix,
@@ -157,9 +162,10 @@ def pool_trippool(xt: np.ndarray, tmap: TileMap, proj: np.ndarray) -> np.ndarray
     tokens are concatenated ("BSAI-ComfyUI-VedaSparse" README, Overview table,
     TripPool row: Avg, Max and Min statistics per tile; Implementation
     section, the TripPool descriptor). Reading: project first, pool after;
-    pads are left out. Returns float64 [n_video, 3r].
+    pads are left out. ``tiles`` as for pool_mean_gate. Returns float64
+    [n_tiles, 3r].
     """
-    x, v = _video_part(xt, tmap)
+    x, v = _tiles_part(xt, tmap, tiles)
     y = x @ np.asarray(proj, dtype=np.float64)            # [n_video, 64, r]
     counts = v.sum(axis=1).astype(np.float64)
     m = v[:, :, None]
@@ -313,17 +319,58 @@ def effective_flops(tmap: TileMap, allow: np.ndarray, d: int) -> int:
 
 
 # --------------------------------------------------------------------------
+# 8. Two-stream budget (reference-to-video)
+# --------------------------------------------------------------------------
+
+def segment_tiles(prefix, segment: int) -> np.ndarray:
+    """Global tile indices of prefix segment ``segment`` (sequence order)."""
+    n = [-(-int(L) // TILE) for L in prefix]
+    t0 = sum(n[:segment])
+    return np.arange(t0, t0 + n[segment], dtype=np.int64)
+
+
+def allowed_two_stream(tmap: TileMap, kv_video, ref_tiles, kv_ref) -> np.ndarray:
+    """bool [n_tiles, n_tiles] under the two-stream budget.
+
+    The reference-to-video predictor keeps, per query tile, a budget of
+    reference tiles and a budget of video tiles, while text and audio
+    conditioning stay dense ("BSAI-ComfyUI-VedaSparse" README, section
+    "v3.4.2 Vendored Official Veda (Pull-and-Go)", R2VA predictor row: two
+    streams of 32 tiles each). Reading: the reference stream is one prefix
+    segment (the reference image), scored against the video query tiles with
+    the same descriptors as the video stream and ranked by the same rule;
+    every other prefix tile stays a dense key; prefix (conditioning) query
+    rows stay dense, including the reference rows. ``kv_ref`` holds, per
+    video query tile, indices into ``ref_tiles``.
+    """
+    npf, n = tmap.n_prefix_tiles, tmap.n_tiles
+    ref_tiles = np.asarray(ref_tiles, dtype=np.int64)
+    allow = np.zeros((n, n), dtype=bool)
+    allow[:npf, :] = True
+    dense_prefix = np.setdiff1d(np.arange(npf), ref_tiles)
+    allow[npf:, dense_prefix] = True
+    for i, (rv, rr) in enumerate(zip(kv_video, kv_ref)):
+        allow[npf + i, npf + np.asarray(rv, dtype=np.int64)] = True
+        allow[npf + i, ref_tiles[np.asarray(rr, dtype=np.int64)]] = True
+    return allow
+
+
+# --------------------------------------------------------------------------
 # The whole path for one (batch, head)
 # --------------------------------------------------------------------------
 
 def head_forward(q, k, v, grid, prefix, shape, sparsity, scorer, wq, wk=None,
-                 scale=None, query_tiles=None, kv_video=None):
+                 scale=None, query_tiles=None, kv_video=None, ref_budget=None,
+                 kv_ref=None):
     """Map -> gather -> pool -> score -> select -> attention for one head.
 
     ``scorer`` is "mean_gate" (``wq`` is the gate; ``wk`` defaults to it) or
     "trippool" (``wq``, ``wk`` are the per-head projections). ``kv_video``
-    overrides the selection (a caller-supplied valid selection). Returns a
-    dict with every intermediate.
+    overrides the selection (a caller-supplied valid selection).
+    ``ref_budget`` = (segment, k_ref) turns on the two-stream budget: that
+    prefix segment's tiles are scored and k_ref of them kept per video query
+    tile (``kv_ref`` overrides that selection). Returns a dict with every
+    intermediate.
     """
     T, Hv, Wv = grid
     d = q.shape[1]
@@ -336,8 +383,19 @@ def head_forward(q, k, v, grid, prefix, shape, sparsity, scorer, wq, wk=None,
     scores = tile_scores(qhat, khat)
     kk = keep_count(sparsity, tmap.n_video_tiles)
     sel = select_topk(scores, kk) if kv_video is None else np.asarray(kv_video)
-    allow = allowed_tiles(tmap, sel)
+    extra = {}
+    if ref_budget is None:
+        allow = allowed_tiles(tmap, sel)
+    else:
+        segment, k_ref = ref_budget
+        ref_tiles = segment_tiles(prefix, segment)
+        khat_ref = pool(kt, tmap, wk, tiles=ref_tiles)
+        ref_scores = tile_scores(qhat, khat_ref)
+        rsel = select_topk(ref_scores, int(k_ref)) if kv_ref is None else np.asarray(kv_ref)
+        allow = allowed_two_stream(tmap, sel, ref_tiles, rsel)
+        extra = {"ref_tiles": ref_tiles, "khat_ref": khat_ref, "ref_scores": ref_scores,
+                 "kv_ref": rsel}
     out, lse = sparse_attention(q, k, v, tmap, allow, scale, query_tiles)
     return {"tmap": tmap, "qt": qt, "kt": kt, "qhat": qhat, "khat": khat,
             "scores": scores, "k": kk, "kv_video": sel, "allow": allow,
-            "out": out, "lse": lse}
+            "out": out, "lse": lse, **extra}

@@ -16,6 +16,7 @@ from tests import test_oracle_attention as ta
 from tests import test_oracle_map as tm_
 from tests import test_oracle_pool_score as tp
 from tests import test_oracle_select as ts
+from tests import test_oracle_two_stream as tts
 
 
 def _map_swapped_xy(T, Hv, Wv, prefix, shape):
@@ -27,14 +28,14 @@ def _map_prefix_shared(T, Hv, Wv, prefix, shape):
     return _orig_tile_map(T, Hv, Wv, (sum(prefix),) if prefix else (), shape)
 
 
-def _pool_mean_with_pads(xt, tmap, gate):
-    x, v = vo._video_part(xt, tmap)
+def _pool_mean_with_pads(xt, tmap, gate, tiles=None):
+    x, v = vo._tiles_part(xt, tmap, tiles)
     return x.mean(axis=1) @ np.asarray(gate, dtype=np.float64)
 
 
-def _trippool_wrong_order(xt, tmap, proj):
+def _trippool_wrong_order(xt, tmap, proj, tiles=None):
     r = np.asarray(proj).shape[1]
-    p = _orig_trippool(xt, tmap, proj)
+    p = _orig_trippool(xt, tmap, proj, tiles)
     return np.concatenate([p[:, r:2 * r], p[:, :r], p[:, 2 * r:]], axis=1)
 
 
@@ -65,6 +66,19 @@ def _allowed_no_prefix_rows(tmap, kv_video):
     return a
 
 
+def _two_stream_reference_dense(tmap, kv_video, ref_tiles, kv_ref):
+    # the budget is ignored: every reference tile stays a dense key
+    a = _orig_two_stream(tmap, kv_video, ref_tiles, kv_ref)
+    a[tmap.n_prefix_tiles:, np.asarray(ref_tiles, dtype=np.int64)] = True
+    return a
+
+
+def _segment_tiles_shifted(prefix, segment):
+    return _orig_segment_tiles(prefix, segment) + 1
+
+
+_orig_two_stream = vo.allowed_two_stream
+_orig_segment_tiles = vo.segment_tiles
 _orig_tile_map = vo.tile_map
 _orig_trippool = vo.pool_trippool
 _orig_scores = vo.tile_scores
@@ -93,6 +107,8 @@ CASES = [
     ("softmax_attention", _softmax_no_scale, ta.test_full_keep_equals_dense),
     ("allowed_tiles", _allowed_no_prefix_rows,
      lambda: ta.test_prefix_rows_are_dense_at_any_sparsity(0.75)),
+    ("allowed_two_stream", _two_stream_reference_dense, tts.test_allowed_sets_by_brute_force),
+    ("segment_tiles", _segment_tiles_shifted, tts.test_segment_tiles_follow_the_tile_map),
 ]
 
 
