@@ -7,19 +7,19 @@
 
 namespace vsa {
 hipError_t launch_attn_bf16(const Plan &p, const void *qt, const void *kt, const void *vt,
-                            const int32_t *s2t, const int32_t *kv_idx, float scale,
-                            void *out, float *lse, hipStream_t stream);
+                            const int32_t *s2t, const int32_t *kv_idx, const int32_t *ref_idx,
+                            float scale, void *out, float *lse, hipStream_t stream);
 hipError_t launch_attn_f32(const Plan &p, const void *qt, const void *kt, const void *vt,
-                           const int32_t *s2t, const int32_t *kv_idx, float scale,
-                           void *out, float *lse, hipStream_t stream);
+                           const int32_t *s2t, const int32_t *kv_idx, const int32_t *ref_idx,
+                           float scale, void *out, float *lse, hipStream_t stream);
 }  // namespace vsa
 
 hipError_t launch_attention(const Plan &p, const void *qt, const void *kt, const void *vt,
-                            const int32_t *s2t, const int32_t *kv_idx, float scale,
-                            void *out, float *lse, hipStream_t stream) {
+                            const int32_t *s2t, const int32_t *kv_idx, const int32_t *ref_idx,
+                            float scale, void *out, float *lse, hipStream_t stream) {
   if (p.dtype == VSA_BF16)
-    return vsa::launch_attn_bf16(p, qt, kt, vt, s2t, kv_idx, scale, out, lse, stream);
-  return vsa::launch_attn_f32(p, qt, kt, vt, s2t, kv_idx, scale, out, lse, stream);
+    return vsa::launch_attn_bf16(p, qt, kt, vt, s2t, kv_idx, ref_idx, scale, out, lse, stream);
+  return vsa::launch_attn_f32(p, qt, kt, vt, s2t, kv_idx, ref_idx, scale, out, lse, stream);
 }
 
 namespace {
@@ -67,11 +67,28 @@ VSA_API int vsa_tile_scores(const vsa_problem *prob, int32_t mode, int32_t proj_
   if (!aligned16(qt) || !aligned16(kt) || ((uintptr_t)pooled_ws & 7u))
     return VSA_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_pool(p, mode, proj_dim, qt, kt, slot_to_token, wq, wk,
-                             (double *)pooled_ws, s);
+  PoolJob job;
+  job.tile0 = p.n_prefix_tiles;
+  job.ntiles = -1;
+  job.rows = p.max_vt;
+  job.src[0] = qt;
+  job.src[1] = kt;
+  job.w[0] = wq;
+  job.w[1] = (mode == VSA_SCORE_MEAN_GATE && !wk) ? wq : wk;
+  hipError_t e = launch_pool(p, mode, proj_dim, job, 2, slot_to_token, (double *)pooled_ws, s);
   if (e != hipSuccess) return VSA_ERR_HIP;
-  int r = mode == VSA_SCORE_MEAN_GATE ? p.d : 3 * proj_dim;
-  return hip_status(launch_scores(p, r, (const double *)pooled_ws, scores, s));
+  const int r = mode == VSA_SCORE_MEAN_GATE ? p.d : 3 * proj_dim;
+  const int64_t bh = (int64_t)p.B * p.H;
+  ScoreJob sj;
+  sj.q = (const double *)pooled_ws;
+  sj.q_bh = (int64_t)p.max_vt * r;
+  sj.k = (const double *)pooled_ws + bh * p.max_vt * r;
+  sj.k_bh = (int64_t)p.max_vt * r;
+  sj.ncols = -1;
+  sj.out = scores;
+  sj.out_row = p.max_vt;
+  sj.out_bh = (int64_t)p.max_vt * p.max_vt;
+  return hip_status(launch_scores(p, r, sj, s));
 }
 
 VSA_API int vsa_select_topk(const vsa_problem *prob, const float *scores, double sparsity,
@@ -80,7 +97,17 @@ VSA_API int vsa_select_topk(const vsa_problem *prob, const float *scores, double
   int st = make_plan(prob, sparsity, &p);
   if (st != VSA_OK) return st;
   if (!scores || !kv_idx) return VSA_ERR_INVALID_ARG;
-  return hip_status(launch_select(p, scores, kv_idx, (hipStream_t)stream));
+  SelectJob j;
+  j.scores = scores;
+  j.in_row = p.max_vt;
+  j.in_bh = (int64_t)p.max_vt * p.max_vt;
+  j.ncols = -1;
+  j.max_cols = p.max_vt;
+  j.k = -1;
+  j.out = kv_idx;
+  j.out_row = p.k_max;
+  j.out_bh = (int64_t)p.max_vt * p.k_max;
+  return hip_status(launch_select(p, j, (hipStream_t)stream));
 }
 
 VSA_API int vsa_sparse_attn_fwd(const vsa_problem *prob, const void *qt, const void *kt,
@@ -97,8 +124,93 @@ VSA_API int vsa_sparse_attn_fwd(const vsa_problem *prob, const void *qt, const v
     return VSA_ERR_INVALID_ARG;
   if (!std::isfinite(softmax_scale)) return VSA_ERR_INVALID_ARG;
   float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)p.d);
-  return hip_status(launch_attention(p, qt, kt, vt, slot_to_token, kv_idx, scale, out, lse,
-                                     (hipStream_t)stream));
+  return hip_status(launch_attention(p, qt, kt, vt, slot_to_token, kv_idx, nullptr, scale, out,
+                                     lse, (hipStream_t)stream));
+}
+
+VSA_API int vsa_ref_scores(const vsa_problem *prob, int32_t mode, int32_t proj_dim,
+                           const void *kt, const int32_t *slot_to_token, const float *wq,
+                           const float *wk, const vsa_ref_budget *budget,
+                           const void *pooled_ws, void *ref_pooled_ws, float *ref_scores,
+                           void *stream) {
+  Plan p;
+  int st = make_plan_geometry(prob, &p);
+  if (st != VSA_OK) return st;
+  st = apply_ref_budget(budget, &p);
+  if (st != VSA_OK) return st;
+  int64_t bytes = 0;
+  st = vsa_pooled_bytes(prob, mode, proj_dim, &bytes);
+  if (st != VSA_OK) return st;
+  if (!kt || !slot_to_token || !wq || !pooled_ws || !ref_pooled_ws || !ref_scores)
+    return VSA_ERR_INVALID_ARG;
+  if (mode == VSA_SCORE_TRIPPOOL && !wk) return VSA_ERR_INVALID_ARG;
+  if (!aligned16(kt) || ((uintptr_t)pooled_ws & 7u) || ((uintptr_t)ref_pooled_ws & 7u))
+    return VSA_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  const float *wkey = (mode == VSA_SCORE_MEAN_GATE && !wk) ? wq : wk;
+  PoolJob job;
+  job.tile0 = p.ref_t0;
+  job.ntiles = p.n_ref;
+  job.rows = p.n_ref;
+  job.src[0] = job.src[1] = kt;
+  job.w[0] = job.w[1] = wkey;
+  hipError_t e = launch_pool(p, mode, proj_dim, job, 1, slot_to_token,
+                             (double *)ref_pooled_ws, s);
+  if (e != hipSuccess) return VSA_ERR_HIP;
+  const int r = mode == VSA_SCORE_MEAN_GATE ? p.d : 3 * proj_dim;
+  ScoreJob sj;
+  sj.q = (const double *)pooled_ws;                  // video query descriptors
+  sj.q_bh = (int64_t)p.max_vt * r;
+  sj.k = (const double *)ref_pooled_ws;
+  sj.k_bh = (int64_t)p.n_ref * r;
+  sj.ncols = p.n_ref;
+  sj.out = ref_scores;
+  sj.out_row = p.n_ref;
+  sj.out_bh = (int64_t)p.max_vt * p.n_ref;
+  return hip_status(launch_scores(p, r, sj, s));
+}
+
+VSA_API int vsa_ref_select(const vsa_problem *prob, const vsa_ref_budget *budget,
+                           const float *ref_scores, int32_t *ref_idx, void *stream) {
+  Plan p;
+  int st = make_plan_geometry(prob, &p);
+  if (st != VSA_OK) return st;
+  st = apply_ref_budget(budget, &p);
+  if (st != VSA_OK) return st;
+  if (!ref_scores || !ref_idx) return VSA_ERR_INVALID_ARG;
+  SelectJob j;
+  j.scores = ref_scores;
+  j.in_row = p.n_ref;
+  j.in_bh = (int64_t)p.max_vt * p.n_ref;
+  j.ncols = p.n_ref;
+  j.max_cols = p.n_ref;
+  j.k = p.k_ref;
+  j.out = ref_idx;
+  j.out_row = p.k_ref;
+  j.out_bh = (int64_t)p.max_vt * p.k_ref;
+  return hip_status(launch_select(p, j, (hipStream_t)stream));
+}
+
+VSA_API int vsa_sparse_attn_fwd_ref(const vsa_problem *prob, const void *qt, const void *kt,
+                                    const void *vt, const int32_t *slot_to_token,
+                                    const int32_t *kv_idx, double sparsity,
+                                    const vsa_ref_budget *budget, const int32_t *ref_idx,
+                                    float softmax_scale, void *out, float *lse,
+                                    void *stream) {
+  Plan p;
+  int st = make_plan(prob, sparsity, &p);
+  if (st != VSA_OK) return st;
+  if (p.dense) return VSA_ERR_INVALID_ARG;
+  st = apply_ref_budget(budget, &p);
+  if (st != VSA_OK) return st;
+  if (!qt || !kt || !vt || !slot_to_token || !out || !kv_idx || !ref_idx)
+    return VSA_ERR_INVALID_ARG;
+  if (!aligned16(qt) || !aligned16(kt) || !aligned16(vt) || !aligned16(out))
+    return VSA_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale)) return VSA_ERR_INVALID_ARG;
+  float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)p.d);
+  return hip_status(launch_attention(p, qt, kt, vt, slot_to_token, kv_idx, ref_idx, scale, out,
+                                     lse, (hipStream_t)stream));
 }
 
 }  // extern "C"

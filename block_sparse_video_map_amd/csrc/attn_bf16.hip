@@ -105,8 +105,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 void attn_bf16_kernel(Plan p, int total, const bf16_bits *__restrict__ qt,
                       const bf16_bits *__restrict__ kt, const bf16_bits *__restrict__ vt,
                       const int32_t *__restrict__ s2t, const int32_t *__restrict__ kv_idx,
-                      float scale_log2, bf16_bits *__restrict__ out,
-                      float *__restrict__ lse) {
+                      const int32_t *__restrict__ ref_idx, float scale_log2,
+                      bf16_bits *__restrict__ out, float *__restrict__ lse) {
   constexpr int NC = D / 16, NDB = D / 32;
   constexpr int UNIT = 32 * D;                 // elements of one unit's K (or V)
   // Two slots, each K then V of one unit. Distinct objects: a slot is only
@@ -126,13 +126,17 @@ void attn_bf16_kernel(Plan p, int total, const bf16_bits *__restrict__ qt,
   const int g = lane / 32, l32 = lane % 32;
   const int npt = p.n_prefix_tiles;
   const bool full_row = p.dense || tq < npt;
-  const int n_kv = full_row ? p.n_tiles[s] : npt + p.k[s];
+  const int n_kv = full_row ? p.n_tiles[s] : video_row_len(p, s);
   // The kept-tile list is read through the constant address space (scalar
   // loads), which keeps it off the vector-memory counter of the copies.
   typedef const __attribute__((address_space(4))) int32_t *const_i32_ptr;
   const const_i32_ptr kv_row =
       full_row ? nullptr
                : (const_i32_ptr)(kv_idx + ((int64_t)bh * p.max_vt + (tq - npt)) * p.k_max);
+  const const_i32_ptr ref_row =
+      (full_row || p.n_ref == 0)
+          ? nullptr
+          : (const_i32_ptr)(ref_idx + ((int64_t)bh * p.max_vt + (tq - npt)) * p.k_ref);
   const int64_t head_base = (int64_t)bh * p.max_tiles;
   const int32_t *map = s2t + (int64_t)s * p.max_tiles * kTile;
 
@@ -159,13 +163,13 @@ void attn_bf16_kernel(Plan p, int total, const bf16_bits *__restrict__ qt,
   auto tile_of = [&](int i, bool &ok) -> int {
     ok = true;
     i = ks + kSplits * i;
-    if (full_row || i < npt) return i;
-    const int j = kv_row[i - npt];
-    if ((unsigned)j >= (unsigned)p.n_vt[s]) {
+    if (full_row) return i;
+    const int tile = video_row_tile(p, s, i, kv_row, ref_row);
+    if (tile < 0) {
       ok = false;
       return 0;
     }
-    return npt + j;
+    return tile;
   };
   // Real-key mask of a tile (bit = slot), ~0 for a full tile.
   auto tile_mask = [&](int tile, bool ok) -> uint64_t {
@@ -361,18 +365,18 @@ void attn_bf16_kernel(Plan p, int total, const bf16_bits *__restrict__ qt,
 }  // namespace
 
 hipError_t launch_attn_bf16(const Plan &p, const void *qt, const void *kt, const void *vt,
-                            const int32_t *s2t, const int32_t *kv_idx, float scale,
-                            void *out, float *lse, hipStream_t stream) {
+                            const int32_t *s2t, const int32_t *kv_idx, const int32_t *ref_idx,
+                            float scale, void *out, float *lse, hipStream_t stream) {
   const int total = (int)(p.tiles_per_batch * p.B);
   const float sl2 = scale * kLog2e;
   if (p.d == 128)
     hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(total), dim3(kThreads), 0, stream, p,
                        total, (const bf16_bits *)qt, (const bf16_bits *)kt,
-                       (const bf16_bits *)vt, s2t, kv_idx, sl2, (bf16_bits *)out, lse);
+                       (const bf16_bits *)vt, s2t, kv_idx, ref_idx, sl2, (bf16_bits *)out, lse);
   else
     hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(total), dim3(kThreads), 0, stream, p,
                        total, (const bf16_bits *)qt, (const bf16_bits *)kt,
-                       (const bf16_bits *)vt, s2t, kv_idx, sl2, (bf16_bits *)out, lse);
+                       (const bf16_bits *)vt, s2t, kv_idx, ref_idx, sl2, (bf16_bits *)out, lse);
   return hipGetLastError();
 }
 

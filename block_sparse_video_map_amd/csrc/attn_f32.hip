@@ -16,6 +16,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(Plan p, const float *__res
                                                       const float *__restrict__ vt,
                                                       const int32_t *__restrict__ s2t,
                                                       const int32_t *__restrict__ kv_idx,
+                                                      const int32_t *__restrict__ ref_idx,
                                                       float scale, float *__restrict__ out,
                                                       float *__restrict__ lse) {
   constexpr int LD = D + 1;
@@ -37,9 +38,12 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(Plan p, const float *__res
   const int lane = threadIdx.x;
   const int npt = p.n_prefix_tiles;
   const bool full_row = p.dense || tq < npt;
-  const int n_kv = full_row ? p.n_tiles[s] : npt + p.k[s];
+  const int n_kv = full_row ? p.n_tiles[s] : video_row_len(p, s);
   const int32_t *kv_row =
       full_row ? nullptr : kv_idx + ((int64_t)bh * p.max_vt + (tq - npt)) * p.k_max;
+  const int32_t *ref_row = (full_row || p.n_ref == 0)
+                               ? nullptr
+                               : ref_idx + ((int64_t)bh * p.max_vt + (tq - npt)) * p.k_ref;
   const int64_t head_base = (int64_t)bh * p.max_tiles;
   const int32_t *map = s2t + (int64_t)s * p.max_tiles * kTile;
 
@@ -54,10 +58,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(Plan p, const float *__res
 
   for (int e = 0; e < n_kv; ++e) {
     int tk = e;
-    if (!full_row && e >= npt) {
-      const int j = kv_row[e - npt];
-      if ((unsigned)j >= (unsigned)p.n_vt[s]) continue;  // not a tile index: ignored
-      tk = npt + j;
+    if (!full_row) {
+      tk = video_row_tile(p, s, e, kv_row, ref_row);
+      if (tk < 0) continue;                              // not a tile index: ignored
     }
     const float *K = kt + (head_base + tk) * (kTile * D);
     const float *V = vt + (head_base + tk) * (kTile * D);
@@ -112,16 +115,17 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(Plan p, const float *__res
 }  // namespace
 
 hipError_t launch_attn_f32(const Plan &p, const void *qt, const void *kt, const void *vt,
-                           const int32_t *s2t, const int32_t *kv_idx, float scale,
+                           const int32_t *s2t, const int32_t *kv_idx, const int32_t *ref_idx,
+                           float scale,
                            void *out, float *lse, hipStream_t stream) {
   const int total = (int)(p.tiles_per_batch * p.B);
   if (p.d == 128)
     hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(total), dim3(64), 0, stream, p,
-                       (const float *)qt, (const float *)kt, (const float *)vt, s2t, kv_idx,
+                       (const float *)qt, (const float *)kt, (const float *)vt, s2t, kv_idx, ref_idx,
                        scale, (float *)out, lse);
   else
     hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(total), dim3(64), 0, stream, p,
-                       (const float *)qt, (const float *)kt, (const float *)vt, s2t, kv_idx,
+                       (const float *)qt, (const float *)kt, (const float *)vt, s2t, kv_idx, ref_idx,
                        scale, (float *)out, lse);
   return hipGetLastError();
 }

@@ -67,6 +67,29 @@ __device__ inline int32_t slot_token(const Plan &p, int s, int tile, int slot) {
   return p.P + (t * p.Hv + y) * p.Wv + x;
 }
 
+// Key tile of entry e of a video query tile's key list: the dense prefix
+// tiles (every prefix tile except those of the reference stream), then the
+// kept reference tiles (ref_row), then the kept video tiles (kv_row). -1 when
+// the stored index is not a tile of its stream (the entry is skipped). With
+// no reference stream (n_ref == 0) the list is all prefix tiles, then kv_row.
+template <typename Ptr>
+__device__ inline int video_row_tile(const Plan &p, int s, int e, Ptr kv_row, Ptr ref_row) {
+  const int n_dense = p.n_prefix_tiles - p.n_ref;
+  if (e < n_dense) return e < p.ref_t0 ? e : e + p.n_ref;
+  e -= n_dense;
+  if (e < p.k_ref) {
+    const int j = ref_row[e];
+    return (unsigned)j < (unsigned)p.n_ref ? p.ref_t0 + j : -1;
+  }
+  const int j = kv_row[e - p.k_ref];
+  return (unsigned)j < (unsigned)p.n_vt[s] ? p.n_prefix_tiles + j : -1;
+}
+
+// Length of a video query tile's key list.
+__device__ inline int video_row_len(const Plan &p, int s) {
+  return p.n_prefix_tiles - p.n_ref + p.k_ref + p.k[s];
+}
+
 // Buffer resource over `bytes` bytes at `base` (raw, untyped loads; reads past
 // the end return zero instead of faulting). The varying part of an address
 // then lives in SGPRs (soffset) plus one per-lane VGPR offset.

@@ -10,13 +10,54 @@ hipError_t launch_build_map(const Plan &p, int32_t *s2t, hipStream_t stream);
 hipError_t launch_gather(const Plan &p, const void *q, const void *k, const void *v,
                          const int32_t *s2t, void *qt, void *kt, void *vt,
                          hipStream_t stream);
-hipError_t launch_pool(const Plan &p, int mode, int proj_dim, const void *qt,
-                       const void *kt, const int32_t *s2t, const float *wq,
-                       const float *wk, double *pooled, hipStream_t stream);
-hipError_t launch_scores(const Plan &p, int r, const double *pooled, float *scores,
-                         hipStream_t stream);
-hipError_t launch_select(const Plan &p, const float *scores, int32_t *kv_idx,
-                         hipStream_t stream);
+// Tiles to pool: per (batch*head), tiles tile0 .. tile0+ntiles-1 of the tiled
+// copies (ntiles < 0: the head's video tiles); source z of the launch reads
+// src[z] with weights w[z] and writes rows ((z*B*H + bh)*rows + i) of the
+// output.
+struct PoolJob {
+  int32_t tile0;
+  int32_t ntiles;
+  int32_t rows;
+  const void *src[2];
+  const float *w[2];
+};
+
+// Descriptor dot products: rows = the head's video query tiles of q, columns
+// = ncols key descriptors of k (ncols < 0: the head's video tiles), output
+// out[bh*out_bh + i*out_row + j]. q_bh / k_bh: doubles per (batch*head).
+struct ScoreJob {
+  const double *q;
+  int64_t q_bh;
+  const double *k;
+  int64_t k_bh;
+  int32_t ncols;
+  float *out;
+  int64_t out_row;
+  int64_t out_bh;
+};
+
+// Top-k per row: row i of (batch*head) bh is scores[bh*in_bh + i*in_row],
+// ncols long (< 0: the head's video tiles), keeping k (< 0: the head's k);
+// the ascending list goes to out[bh*out_bh + i*out_row], padded with -1 up
+// to out_row.
+struct SelectJob {
+  const float *scores;
+  int64_t in_row;
+  int64_t in_bh;
+  int32_t ncols;
+  int32_t max_cols;
+  int32_t k;
+  int32_t *out;
+  int32_t out_row;
+  int64_t out_bh;
+};
+
+hipError_t launch_pool(const Plan &p, int mode, int proj_dim, const PoolJob &job, int nsrc,
+                       const int32_t *s2t, double *pooled, hipStream_t stream);
+hipError_t launch_scores(const Plan &p, int r, const ScoreJob &job, hipStream_t stream);
+hipError_t launch_select(const Plan &p, const SelectJob &job, hipStream_t stream);
+// ref_idx: the reference stream's kept tiles when p.n_ref > 0, else unused.
 hipError_t launch_attention(const Plan &p, const void *qt, const void *kt,
                             const void *vt, const int32_t *s2t, const int32_t *kv_idx,
-                            float scale, void *out, float *lse, hipStream_t stream);
+                            const int32_t *ref_idx, float scale, void *out, float *lse,
+                            hipStream_t stream);

@@ -53,6 +53,7 @@ int make_plan_geometry(const vsa_problem *prob, Plan *p) {
 
   p->n_shapes = prob->n_shapes;
   p->max_tiles = p->max_vt = 0;
+  p->ref_t0 = p->n_ref = p->k_ref = 0;
   for (int s = 0; s < prob->n_shapes; ++s) {
     int32_t pt = prob->tile_shape[3 * s], ph = prob->tile_shape[3 * s + 1],
             pw = prob->tile_shape[3 * s + 2];
@@ -92,6 +93,19 @@ int make_plan(const vsa_problem *prob, double sparsity, Plan *p) {
     p->k[s] = (int32_t)kk;
     if (p->k[s] > p->k_max) p->k_max = p->k[s];
   }
+  return VSA_OK;
+}
+
+int apply_ref_budget(const vsa_ref_budget *rb, Plan *p) {
+  if (!rb) return VSA_ERR_INVALID_ARG;
+  if (rb->segment < 0 || rb->segment >= p->n_prefix) return VSA_ERR_INVALID_ARG;
+  const int t0 = p->prefix_tile0[rb->segment];
+  const int n = p->prefix_tile0[rb->segment + 1] - t0;
+  if (n < 1) return VSA_ERR_INVALID_ARG;
+  if (rb->k_ref < 1 || rb->k_ref > n) return VSA_ERR_INVALID_ARG;
+  p->ref_t0 = t0;
+  p->n_ref = n;
+  p->k_ref = rb->k_ref;
   return VSA_OK;
 }
 
@@ -144,18 +158,14 @@ VSA_API int vsa_pooled_bytes(const vsa_problem *prob, int32_t mode, int32_t proj
   return VSA_OK;
 }
 
-VSA_API int vsa_kept_stats(const vsa_problem *prob, double sparsity, int64_t *kept,
-                           double *frac) {
-  if (!kept || !frac) return VSA_ERR_INVALID_ARG;
-  Plan p;
-  int st = make_plan(prob, sparsity, &p);
-  if (st != VSA_OK) return st;
+static int kept_stats(const Plan &p, int64_t *kept, double *frac) {
   int64_t k_sum = 0, full = 0;
   for (int h = 0; h < p.H; ++h) {
     int s = h % p.n_shapes;
     int64_t nt = p.n_tiles[s], npt = p.n_prefix_tiles, nv = p.n_vt[s];
     int64_t kk = p.dense ? nv : p.k[s];
-    k_sum += npt * nt + nv * (npt + kk);
+    int64_t row = p.dense ? nt : npt - p.n_ref + p.k_ref + kk;
+    k_sum += npt * nt + nv * row;
     full += nt * nt;
   }
   *kept = k_sum * p.B;
@@ -163,13 +173,29 @@ VSA_API int vsa_kept_stats(const vsa_problem *prob, double sparsity, int64_t *ke
   return VSA_OK;
 }
 
-VSA_API int vsa_count_flops(const vsa_problem *prob, double sparsity,
-                            const int32_t *s2t, const int32_t *kv_idx, double *flops) {
-  if (!s2t || !flops) return VSA_ERR_INVALID_ARG;
+VSA_API int vsa_kept_stats(const vsa_problem *prob, double sparsity, int64_t *kept,
+                           double *frac) {
+  if (!kept || !frac) return VSA_ERR_INVALID_ARG;
   Plan p;
   int st = make_plan(prob, sparsity, &p);
   if (st != VSA_OK) return st;
-  if (!p.dense && !kv_idx) return VSA_ERR_INVALID_ARG;
+  return kept_stats(p, kept, frac);
+}
+
+VSA_API int vsa_kept_stats_ref(const vsa_problem *prob, double sparsity,
+                               const vsa_ref_budget *budget, int64_t *kept, double *frac) {
+  if (!kept || !frac) return VSA_ERR_INVALID_ARG;
+  Plan p;
+  int st = make_plan(prob, sparsity, &p);
+  if (st != VSA_OK) return st;
+  if (p.dense) return VSA_ERR_INVALID_ARG;
+  st = apply_ref_budget(budget, &p);
+  if (st != VSA_OK) return st;
+  return kept_stats(p, kept, frac);
+}
+
+static int count_flops(const Plan &p, const int32_t *s2t, const int32_t *kv_idx,
+                       const int32_t *ref_idx, double *flops) {
   long double total = 0;
   int npt = p.n_prefix_tiles;
   for (int b = 0; b < p.B; ++b) {
@@ -187,7 +213,17 @@ VSA_API int vsa_count_flops(const vsa_problem *prob, double sparsity,
           keys = p.N;
         } else {
           keys = p.P;
-          const int32_t *row = kv_idx + (((int64_t)b * p.H + h) * p.max_vt + (t - npt)) * p.k_max;
+          const int64_t qrow = ((int64_t)b * p.H + h) * p.max_vt + (t - npt);
+          if (p.n_ref > 0) {
+            for (int j = 0; j < p.n_ref; ++j) keys -= real(p.ref_t0 + j);
+            const int32_t *rrow = ref_idx + qrow * p.k_ref;
+            for (int e = 0; e < p.k_ref; ++e) {
+              int32_t j = rrow[e];
+              if (j < 0 || j >= p.n_ref) return VSA_ERR_INVALID_ARG;
+              keys += real(p.ref_t0 + j);
+            }
+          }
+          const int32_t *row = kv_idx + qrow * p.k_max;
           for (int e = 0; e < p.k[s]; ++e) {
             int32_t j = row[e];
             if (j < 0 || j >= p.n_vt[s]) return VSA_ERR_INVALID_ARG;
@@ -199,6 +235,61 @@ VSA_API int vsa_count_flops(const vsa_problem *prob, double sparsity,
     }
   }
   *flops = (double)(total * 4.0L * p.d);
+  return VSA_OK;
+}
+
+VSA_API int vsa_count_flops(const vsa_problem *prob, double sparsity,
+                            const int32_t *s2t, const int32_t *kv_idx, double *flops) {
+  if (!s2t || !flops) return VSA_ERR_INVALID_ARG;
+  Plan p;
+  int st = make_plan(prob, sparsity, &p);
+  if (st != VSA_OK) return st;
+  if (!p.dense && !kv_idx) return VSA_ERR_INVALID_ARG;
+  return count_flops(p, s2t, kv_idx, nullptr, flops);
+}
+
+VSA_API int vsa_count_flops_ref(const vsa_problem *prob, double sparsity,
+                                const vsa_ref_budget *budget, const int32_t *s2t,
+                                const int32_t *kv_idx, const int32_t *ref_idx, double *flops) {
+  if (!s2t || !flops || !kv_idx || !ref_idx) return VSA_ERR_INVALID_ARG;
+  Plan p;
+  int st = make_plan(prob, sparsity, &p);
+  if (st != VSA_OK) return st;
+  if (p.dense) return VSA_ERR_INVALID_ARG;
+  st = apply_ref_budget(budget, &p);
+  if (st != VSA_OK) return st;
+  return count_flops(p, s2t, kv_idx, ref_idx, flops);
+}
+
+VSA_API int vsa_ref_sizes(const vsa_problem *prob, const vsa_ref_budget *budget,
+                          int32_t *n_ref_tiles, int64_t *ref_score_elems,
+                          int64_t *ref_idx_elems) {
+  if (!n_ref_tiles || !ref_score_elems || !ref_idx_elems) return VSA_ERR_INVALID_ARG;
+  Plan p;
+  int st = make_plan_geometry(prob, &p);
+  if (st != VSA_OK) return st;
+  st = apply_ref_budget(budget, &p);
+  if (st != VSA_OK) return st;
+  const int64_t bh = (int64_t)p.B * p.H;
+  *n_ref_tiles = p.n_ref;
+  *ref_score_elems = bh * p.max_vt * p.n_ref;
+  *ref_idx_elems = bh * p.max_vt * p.k_ref;
+  return VSA_OK;
+}
+
+VSA_API int vsa_ref_pooled_bytes(const vsa_problem *prob, int32_t mode, int32_t proj_dim,
+                                 const vsa_ref_budget *budget, int64_t *bytes) {
+  if (!bytes) return VSA_ERR_INVALID_ARG;
+  int64_t full = 0;
+  int st = vsa_pooled_bytes(prob, mode, proj_dim, &full);
+  if (st != VSA_OK) return st;
+  Plan p;
+  st = make_plan_geometry(prob, &p);
+  if (st != VSA_OK) return st;
+  st = apply_ref_budget(budget, &p);
+  if (st != VSA_OK) return st;
+  const int64_t r = full / (2 * (int64_t)p.B * p.H * p.max_vt * (int64_t)sizeof(double));
+  *bytes = (int64_t)p.B * p.H * p.n_ref * r * (int64_t)sizeof(double);
   return VSA_OK;
 }
 

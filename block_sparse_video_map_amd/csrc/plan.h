@@ -24,6 +24,10 @@ struct Plan {
   int32_t k[VSA_MAX_SHAPES];
   int32_t max_tiles, max_vt, k_max, keep_bp;
   int32_t dense;                               // sparsity == 0
+  // Two-stream budget: prefix tiles [ref_t0, ref_t0 + n_ref) form the
+  // reference stream, of which every video query tile keeps k_ref
+  // (n_ref == 0: off, every prefix tile is a dense key).
+  int32_t ref_t0, n_ref, k_ref;
   int64_t tiles_per_batch;                     // sum over heads of n_tiles
   int64_t tiles_per_cycle;                     // sum over one shape cycle
 };
@@ -33,3 +37,6 @@ int make_plan(const vsa_problem *prob, double sparsity, Plan *plan);
 
 // Validates `prob` ignoring sparsity (steps that do not depend on it).
 int make_plan_geometry(const vsa_problem *prob, Plan *plan);
+
+// Validates a two-stream budget against the plan and records it there.
+int apply_ref_budget(const vsa_ref_budget *budget, Plan *plan);

@@ -62,9 +62,7 @@ __device__ inline void load8_f32<float>(const float *__restrict__ src, float (&v
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void pool_mean_gate_kernel(
-    Plan p, const T *__restrict__ qt, const T *__restrict__ kt,
-    const int32_t *__restrict__ s2t, const float *__restrict__ wq,
-    const float *__restrict__ wk, double *__restrict__ pooled) {
+    Plan p, PoolJob job, const int32_t *__restrict__ s2t, double *__restrict__ pooled) {
   constexpr int NV = kTile * D / 8;          // 8-element vectors per tile
   constexpr int VPT = NV / 256;              // vectors per thread (4 for D=128)
   static_assert(VPT >= 1 && NV % 256 == 0, "tile must split evenly over 256 threads");
@@ -75,18 +73,18 @@ __global__ __launch_bounds__(256) void pool_mean_gate_kernel(
 
   const int bh = blockIdx.y, which = blockIdx.z;
   const int h = bh % p.H, s = h % p.n_shapes;
-  const int n = p.n_vt[s];
+  const int n = job.ntiles < 0 ? p.n_vt[s] : job.ntiles;
   const int vt0 = blockIdx.x * kPoolTiles;
   if (vt0 >= n) return;
   const int nt = min(kPoolTiles, n - vt0);
-  const T *src = (which == 0 ? qt : kt) + ((int64_t)bh * p.max_tiles + p.n_prefix_tiles + vt0) *
-                                              (kTile * D);
-  const float *w = (which == 0 || !wk ? wq : wk) + (int64_t)h * D * D;
+  const T *src = (const T *)job.src[which] +
+                 ((int64_t)bh * p.max_tiles + job.tile0 + vt0) * (kTile * D);
+  const float *w = job.w[which] + (int64_t)h * D * D;
   const int t = threadIdx.x, lane = t % 64, wave = t / 64;
 
   // Real-slot counts: wave w counts tiles w, w+4, ... (one slot per lane).
   for (int tt = wave; tt < nt; tt += 4) {
-    const int tok = s2t[((int64_t)s * p.max_tiles + p.n_prefix_tiles + vt0 + tt) * kTile + lane];
+    const int tok = s2t[((int64_t)s * p.max_tiles + job.tile0 + vt0 + tt) * kTile + lane];
     const int c = __popcll(__ballot(tok >= 0));
     if (lane == 0) count[tt] = c;
   }
@@ -131,7 +129,7 @@ __global__ __launch_bounds__(256) void pool_mean_gate_kernel(
   // Gate product on the f64 MFMA. A: lane l holds mean[l%16][k0 + l/16];
   // B: gate[k0 + l/16][col0 + l%16]; D element e: row 4e + l/16, column l%16.
   const int l16 = lane % 16, g4 = lane / 16;
-  double *dst = pooled + (((int64_t)which * p.B * p.H + bh) * p.max_vt + vt0) * D;
+  double *dst = pooled + (((int64_t)which * p.B * p.H + bh) * job.rows + vt0) * D;
   for (int cb = wave; cb < D / 16; cb += 4) {
     f64x4 acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll 8
@@ -157,9 +155,7 @@ __global__ __launch_bounds__(256) void pool_mean_gate_kernel(
 // (l % 16); the statistics are reduced across lanes, then across waves.
 template <typename T, int D, int R>
 __global__ __launch_bounds__(256) void pool_trippool_kernel(
-    Plan p, const T *__restrict__ qt, const T *__restrict__ kt,
-    const int32_t *__restrict__ s2t, const float *__restrict__ wq,
-    const float *__restrict__ wk, double *__restrict__ pooled) {
+    Plan p, PoolJob job, const int32_t *__restrict__ s2t, double *__restrict__ pooled) {
   constexpr int LD = D + 4;                  // float rows, 16-byte aligned
   constexpr int RB = (R + 15) / 16;          // 16-column blocks
   __shared__ __attribute__((aligned(16))) float xs[kTile * LD];
@@ -169,10 +165,10 @@ __global__ __launch_bounds__(256) void pool_trippool_kernel(
 
   const int vt_i = blockIdx.x, bh = blockIdx.y, which = blockIdx.z;
   const int h = bh % p.H, s = h % p.n_shapes;
-  if (vt_i >= p.n_vt[s]) return;
-  const int tile = p.n_prefix_tiles + vt_i;
-  const T *src = (which == 0 ? qt : kt) + ((int64_t)bh * p.max_tiles + tile) * (kTile * D);
-  const float *w = (which == 0 ? wq : wk) + (int64_t)h * D * R;
+  if (vt_i >= (job.ntiles < 0 ? p.n_vt[s] : job.ntiles)) return;
+  const int tile = job.tile0 + vt_i;
+  const T *src = (const T *)job.src[which] + ((int64_t)bh * p.max_tiles + tile) * (kTile * D);
+  const float *w = job.w[which] + (int64_t)h * D * R;
 
   if (threadIdx.x < kTile)
     valid[threadIdx.x] = s2t[((int64_t)s * p.max_tiles + tile) * kTile + threadIdx.x] >= 0;
@@ -244,7 +240,7 @@ __global__ __launch_bounds__(256) void pool_trippool_kernel(
       tx = fmax(tx, red[1][ww][j]);
       tn = fmin(tn, red[2][ww][j]);
     }
-    double *out = pooled + (((int64_t)which * p.B * p.H + bh) * p.max_vt + vt_i) * (3 * R);
+    double *out = pooled + (((int64_t)which * p.B * p.H + bh) * job.rows + vt_i) * (3 * R);
     out[j] = ts / (double)n;
     out[R + j] = tx;
     out[2 * R + j] = tn;
@@ -266,25 +262,24 @@ constexpr int kLK = kKC + 2;   // padded LDS row (doubles)
 // of Qd and Kd are staged through LDS in chunks of 16 contraction columns,
 // double-buffered: every thread fetches 4 doubles of each for the next chunk
 // while the current chunk is multiplied.
-__global__ __launch_bounds__(256) void scores_kernel(Plan p, int r,
-                                                     const double *__restrict__ pooled,
-                                                     float *__restrict__ scores) {
+__global__ __launch_bounds__(256) void scores_kernel(Plan p, int r, ScoreJob job) {
   __shared__ double As[2][kSB * kLK];
   __shared__ double Bs[2][kSB * kLK];
   const int bh = blockIdx.z, h = bh % p.H, s = h % p.n_shapes;
-  const int n = p.n_vt[s];
+  const int n = p.n_vt[s];                                   // query rows
+  const int m = job.ncols < 0 ? n : job.ncols;               // key columns
   const int i0 = blockIdx.y * kSB, j0 = blockIdx.x * kSB;
-  if (i0 >= n || j0 >= n) return;
+  if (i0 >= n || j0 >= m) return;
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t / 64);
   const int lane = t % 64, g = lane / 16, l16 = lane % 16;
   const int wr = (wave / 2) * 32, wc = (wave % 2) * 32;    // wave's block inside the 64x64
-  const double *Qd = pooled + (int64_t)bh * p.max_vt * r;
-  const double *Kd = pooled + ((int64_t)p.B * p.H + bh) * p.max_vt * r;
+  const double *Qd = job.q + (int64_t)bh * job.q_bh;
+  const double *Kd = job.k + (int64_t)bh * job.k_bh;
 
   // Thread t stages row t/4, columns 4*(t%4) .. +3 of the chunk, for A and B.
   const int srow = t / 4, scol = (t % 4) * 4;
-  const bool oka = i0 + srow < n, okb = j0 + srow < n;
+  const bool oka = i0 + srow < n, okb = j0 + srow < m;
   const double *qa = Qd + (int64_t)(i0 + srow) * r + scol;
   const double *kb = Kd + (int64_t)(j0 + srow) * r + scol;
   double ra[4], rb[4];
@@ -336,7 +331,7 @@ __global__ __launch_bounds__(256) void scores_kernel(Plan p, int r,
     __syncthreads();
   }
   // D element e of lane l is row 4*e + l/16, column l % 16 of the block.
-  float *out = scores + (int64_t)bh * p.max_vt * p.max_vt;
+  float *out = job.out + (int64_t)bh * job.out_bh;
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -344,25 +339,25 @@ __global__ __launch_bounds__(256) void scores_kernel(Plan p, int r,
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = i0 + wr + a * 16 + 4 * e + g, j = j0 + wc + b * 16 + l16;
-        if (i < n && j < n) out[(int64_t)i * p.max_vt + j] = (float)acc[a][b][e];
+        if (i < n && j < m) out[(int64_t)i * job.out_row + j] = (float)acc[a][b][e];
       }
 }
 
 template <typename T, int D>
-hipError_t pool_t(const Plan &p, int mode, int R, const void *qt, const void *kt,
-                  const int32_t *s2t, const float *wq, const float *wk, double *pooled,
-                  hipStream_t st) {
-  dim3 grid(p.max_vt, p.B * p.H, 2);
+hipError_t pool_t(const Plan &p, int mode, int R, const PoolJob &job, int nsrc,
+                  const int32_t *s2t, double *pooled, hipStream_t st) {
+  const int rows = job.ntiles < 0 ? p.max_vt : job.ntiles;
+  dim3 grid(rows, p.B * p.H, nsrc);
   if (mode == VSA_SCORE_MEAN_GATE) {
-    dim3 grid_mg((p.max_vt + kPoolTiles - 1) / kPoolTiles, p.B * p.H, 2);
-    hipLaunchKernelGGL((pool_mean_gate_kernel<T, D>), grid_mg, dim3(256), 0, st, p,
-                       (const T *)qt, (const T *)kt, s2t, wq, wk, pooled);
+    dim3 grid_mg((rows + kPoolTiles - 1) / kPoolTiles, p.B * p.H, nsrc);
+    hipLaunchKernelGGL((pool_mean_gate_kernel<T, D>), grid_mg, dim3(256), 0, st, p, job, s2t,
+                       pooled);
   } else {
     switch (R) {
 #define VSA_TRIP(RR)                                                                    \
   case RR:                                                                              \
-    hipLaunchKernelGGL((pool_trippool_kernel<T, D, RR>), grid, dim3(256), 0, st, p,     \
-                       (const T *)qt, (const T *)kt, s2t, wq, wk, pooled);               \
+    hipLaunchKernelGGL((pool_trippool_kernel<T, D, RR>), grid, dim3(256), 0, st, p, job, \
+                       s2t, pooled);                                                     \
     break;
       VSA_TRIP(8) VSA_TRIP(16) VSA_TRIP(32) VSA_TRIP(64)
 #undef VSA_TRIP
@@ -375,23 +370,21 @@ hipError_t pool_t(const Plan &p, int mode, int R, const void *qt, const void *kt
 }  // namespace
 }  // namespace vsa
 
-hipError_t launch_pool(const Plan &p, int mode, int proj_dim, const void *qt,
-                       const void *kt, const int32_t *s2t, const float *wq,
-                       const float *wk, double *pooled, hipStream_t stream) {
+hipError_t launch_pool(const Plan &p, int mode, int proj_dim, const PoolJob &job, int nsrc,
+                       const int32_t *s2t, double *pooled, hipStream_t stream) {
   if (p.dtype == VSA_BF16) {
     if (p.d == 128)
-      return vsa::pool_t<bf16_bits, 128>(p, mode, proj_dim, qt, kt, s2t, wq, wk, pooled, stream);
-    return vsa::pool_t<bf16_bits, 64>(p, mode, proj_dim, qt, kt, s2t, wq, wk, pooled, stream);
+      return vsa::pool_t<bf16_bits, 128>(p, mode, proj_dim, job, nsrc, s2t, pooled, stream);
+    return vsa::pool_t<bf16_bits, 64>(p, mode, proj_dim, job, nsrc, s2t, pooled, stream);
   }
   if (p.d == 128)
-    return vsa::pool_t<float, 128>(p, mode, proj_dim, qt, kt, s2t, wq, wk, pooled, stream);
-  return vsa::pool_t<float, 64>(p, mode, proj_dim, qt, kt, s2t, wq, wk, pooled, stream);
+    return vsa::pool_t<float, 128>(p, mode, proj_dim, job, nsrc, s2t, pooled, stream);
+  return vsa::pool_t<float, 64>(p, mode, proj_dim, job, nsrc, s2t, pooled, stream);
 }
 
-hipError_t launch_scores(const Plan &p, int r, const double *pooled, float *scores,
-                         hipStream_t stream) {
-  int nb = (p.max_vt + vsa::kSB - 1) / vsa::kSB;
-  dim3 grid(nb, nb, p.B * p.H);
-  hipLaunchKernelGGL(vsa::scores_kernel, grid, dim3(256), 0, stream, p, r, pooled, scores);
+hipError_t launch_scores(const Plan &p, int r, const ScoreJob &job, hipStream_t stream) {
+  const int cols = job.ncols < 0 ? p.max_vt : job.ncols;
+  dim3 grid((cols + vsa::kSB - 1) / vsa::kSB, (p.max_vt + vsa::kSB - 1) / vsa::kSB, p.B * p.H);
+  hipLaunchKernelGGL(vsa::scores_kernel, grid, dim3(256), 0, stream, p, r, job);
   return hipGetLastError();
 }

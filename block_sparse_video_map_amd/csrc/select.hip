@@ -47,21 +47,19 @@ __device__ inline int block_exclusive_scan(int v, int *wave_tot, int &total) {
 
 // E = keys per thread (n <= E * kSelThreads).
 template <int E>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(Plan p,
-                                                             const float *__restrict__ scores,
-                                                             int32_t *__restrict__ kv_idx) {
+__global__ __launch_bounds__(kSelThreads) void select_kernel(Plan p, SelectJob job) {
   __shared__ int hist[256];
   __shared__ int wave_tot[kSelWaves];
   __shared__ int sel_bin, sel_above;
 
   const int i = blockIdx.x, bh = blockIdx.y, h = bh % p.H, s = h % p.n_shapes;
-  const int n = p.n_vt[s];
-  if (i >= n) return;
-  const int k = p.k[s];
+  if (i >= p.n_vt[s]) return;                   // one row per video query tile
+  const int n = job.ncols < 0 ? p.n_vt[s] : job.ncols;
+  const int k = job.k < 0 ? p.k[s] : job.k;
   const int t = threadIdx.x;
   const int j0 = t * E;                         // this thread's first index
 
-  const float *row = scores + ((int64_t)bh * p.max_vt + i) * p.max_vt;
+  const float *row = job.scores + (int64_t)bh * job.in_bh + (int64_t)i * job.in_row;
   uint32_t key[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) key[e] = (j0 + e < n) ? order_key(row[j0 + e]) : 0u;
@@ -113,7 +111,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Plan p,
   }
   int tot_keep;
   int pos = block_exclusive_scan(n_keep, wave_tot, tot_keep);   // tot_keep == k
-  int32_t *out = kv_idx + ((int64_t)bh * p.max_vt + i) * p.k_max;
+  int32_t *out = job.out + (int64_t)bh * job.out_bh + (int64_t)i * job.out_row;
   eq_rank -= n_eq;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -126,24 +124,23 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Plan p,
       if (keep) out[pos++] = j0 + e;
     }
   }
-  for (int c = k + t; c < p.k_max; c += kSelThreads) out[c] = -1;
+  for (int c = k + t; c < job.out_row; c += kSelThreads) out[c] = -1;
 }
 
 }  // namespace
 }  // namespace vsa
 
-hipError_t launch_select(const Plan &p, const float *scores, int32_t *kv_idx,
-                         hipStream_t stream) {
+hipError_t launch_select(const Plan &p, const SelectJob &job, hipStream_t stream) {
   dim3 grid(p.max_vt, p.B * p.H);
   dim3 block(vsa::kSelThreads);
-  const int e = (p.max_vt + vsa::kSelThreads - 1) / vsa::kSelThreads;
+  const int e = (job.max_cols + vsa::kSelThreads - 1) / vsa::kSelThreads;
   if (e <= 4)
-    hipLaunchKernelGGL(vsa::select_kernel<4>, grid, block, 0, stream, p, scores, kv_idx);
+    hipLaunchKernelGGL(vsa::select_kernel<4>, grid, block, 0, stream, p, job);
   else if (e <= 8)
-    hipLaunchKernelGGL(vsa::select_kernel<8>, grid, block, 0, stream, p, scores, kv_idx);
+    hipLaunchKernelGGL(vsa::select_kernel<8>, grid, block, 0, stream, p, job);
   else if (e <= 16)
-    hipLaunchKernelGGL(vsa::select_kernel<16>, grid, block, 0, stream, p, scores, kv_idx);
+    hipLaunchKernelGGL(vsa::select_kernel<16>, grid, block, 0, stream, p, job);
   else
-    hipLaunchKernelGGL(vsa::select_kernel<32>, grid, block, 0, stream, p, scores, kv_idx);
+    hipLaunchKernelGGL(vsa::select_kernel<32>, grid, block, 0, stream, p, job);
   return hipGetLastError();
 }

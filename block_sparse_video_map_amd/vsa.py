@@ -28,7 +28,9 @@ VSA_MAX_VIDEO_TILES, VSA_MAX_PROJ = 8192, 64
 # Names declared in include/vsa.h.
 EXPORTS = ("vsa_query_sizes", "vsa_pooled_bytes", "vsa_map_tiles", "vsa_tile_scores",
            "vsa_select_topk", "vsa_sparse_attn_fwd", "vsa_kept_stats",
-           "vsa_count_flops", "vsa_status_string", "vsa_version")
+           "vsa_count_flops", "vsa_ref_sizes", "vsa_ref_pooled_bytes", "vsa_ref_scores",
+           "vsa_ref_select", "vsa_sparse_attn_fwd_ref", "vsa_kept_stats_ref",
+           "vsa_count_flops_ref", "vsa_status_string", "vsa_version")
 
 
 class vsa_problem(ctypes.Structure):
@@ -53,6 +55,10 @@ class vsa_sizes(ctypes.Structure):
                 ("k", ctypes.c_int32 * VSA_MAX_SHAPES)]
 
 
+class vsa_ref_budget(ctypes.Structure):
+    _fields_ = [("segment", ctypes.c_int32), ("k_ref", ctypes.c_int32)]
+
+
 class VSAError(RuntimeError):
     def __init__(self, fn: str, status: int):
         self.status = status
@@ -72,6 +78,7 @@ def lib() -> ctypes.CDLL:
                 "`python -m block_sparse_video_map_amd.build` (no fallback exists)")
         L = ctypes.CDLL(LIB_PATH)
         P, S = ctypes.POINTER(vsa_problem), ctypes.POINTER(vsa_sizes)
+        R = ctypes.POINTER(vsa_ref_budget)
         vp, i32, i64, f64, f32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
                                   ctypes.c_double, ctypes.c_float)
         sig = {
@@ -83,6 +90,14 @@ def lib() -> ctypes.CDLL:
             "vsa_sparse_attn_fwd": [P, vp, vp, vp, vp, vp, f64, f32, vp, vp, vp],
             "vsa_kept_stats": [P, f64, ctypes.POINTER(i64), ctypes.POINTER(f64)],
             "vsa_count_flops": [P, f64, vp, vp, ctypes.POINTER(f64)],
+            "vsa_ref_sizes": [P, R, ctypes.POINTER(i32), ctypes.POINTER(i64),
+                              ctypes.POINTER(i64)],
+            "vsa_ref_pooled_bytes": [P, i32, i32, R, ctypes.POINTER(i64)],
+            "vsa_ref_scores": [P, i32, i32, vp, vp, vp, vp, R, vp, vp, vp, vp],
+            "vsa_ref_select": [P, R, vp, vp, vp],
+            "vsa_sparse_attn_fwd_ref": [P, vp, vp, vp, vp, vp, f64, R, vp, f32, vp, vp, vp],
+            "vsa_kept_stats_ref": [P, f64, R, ctypes.POINTER(i64), ctypes.POINTER(f64)],
+            "vsa_count_flops_ref": [P, f64, R, vp, vp, vp, ctypes.POINTER(f64)],
             "vsa_status_string": [ctypes.c_int],
             "vsa_version": [],
         }
@@ -259,6 +274,92 @@ def vsa_sparse_attn_fwd(prob: Problem, qt, kt, vt, slot_to_token, kv_idx, sparsi
         float(sparsity), float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream)))
 
 
+# ---------------------------------------------------- two-stream budget calls
+
+def ref_budget(segment: int, k_ref: int) -> vsa_ref_budget:
+    return vsa_ref_budget(int(segment), int(k_ref))
+
+
+def vsa_ref_sizes(prob: Problem, budget: vsa_ref_budget):
+    n, se, ie = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
+    _check("vsa_ref_sizes", lib().vsa_ref_sizes(prob.ref, ctypes.byref(budget), ctypes.byref(n),
+                                                ctypes.byref(se), ctypes.byref(ie)))
+    return n.value, se.value, ie.value
+
+
+def vsa_ref_pooled_bytes(prob: Problem, mode: int, proj_dim: int, budget: vsa_ref_budget) -> int:
+    b = ctypes.c_int64()
+    _check("vsa_ref_pooled_bytes", lib().vsa_ref_pooled_bytes(
+        prob.ref, int(mode), int(proj_dim), ctypes.byref(budget), ctypes.byref(b)))
+    return b.value
+
+
+def vsa_ref_scores(prob: Problem, mode: int, proj_dim: int, kt, slot_to_token, wq, wk,
+                   budget: vsa_ref_budget, pooled_ws, ref_pooled_ws, ref_scores, stream=None):
+    import torch
+    _, se, _ = vsa_ref_sizes(prob, budget)
+    _need(ref_scores, se, torch.float32, "ref_scores")
+    _need(wq, 1, torch.float32, "wq")
+    _need(wk, 1, torch.float32, "wk")
+    if pooled_ws.numel() * pooled_ws.element_size() < vsa_pooled_bytes(prob, mode, proj_dim):
+        raise ValueError("pooled_ws too small")
+    if (ref_pooled_ws.numel() * ref_pooled_ws.element_size()
+            < vsa_ref_pooled_bytes(prob, mode, proj_dim, budget)):
+        raise ValueError("ref_pooled_ws too small")
+    _check("vsa_ref_scores", lib().vsa_ref_scores(
+        prob.ref, int(mode), int(proj_dim), _ptr(kt), _ptr(slot_to_token), _ptr(wq), _ptr(wk),
+        ctypes.byref(budget), _ptr(pooled_ws), _ptr(ref_pooled_ws), _ptr(ref_scores),
+        _stream(stream)))
+
+
+def vsa_ref_select(prob: Problem, budget: vsa_ref_budget, ref_scores, ref_idx, stream=None):
+    import torch
+    _, se, ie = vsa_ref_sizes(prob, budget)
+    _need(ref_scores, se, torch.float32, "ref_scores")
+    _need(ref_idx, ie, torch.int32, "ref_idx")
+    _check("vsa_ref_select", lib().vsa_ref_select(
+        prob.ref, ctypes.byref(budget), _ptr(ref_scores), _ptr(ref_idx), _stream(stream)))
+
+
+def vsa_sparse_attn_fwd_ref(prob: Problem, qt, kt, vt, slot_to_token, kv_idx, sparsity: float,
+                            budget: vsa_ref_budget, ref_idx, softmax_scale: float, out,
+                            lse=None, stream=None):
+    import torch
+    sz = vsa_query_sizes(prob, sparsity)
+    _, _, ie = vsa_ref_sizes(prob, budget)
+    et = _elem_dtype(prob)
+    for name, x in (("qt", qt), ("kt", kt), ("vt", vt)):
+        _need(x, sz.tiled_elems, et, name)
+    _need(out, sz.out_elems, et, "out")
+    _need(lse, prob.B * prob.H * prob.N, torch.float32, "lse")
+    _need(kv_idx, sz.idx_elems, torch.int32, "kv_idx")
+    _need(ref_idx, ie, torch.int32, "ref_idx")
+    _check("vsa_sparse_attn_fwd_ref", lib().vsa_sparse_attn_fwd_ref(
+        prob.ref, _ptr(qt), _ptr(kt), _ptr(vt), _ptr(slot_to_token), _ptr(kv_idx),
+        float(sparsity), ctypes.byref(budget), _ptr(ref_idx), float(softmax_scale), _ptr(out),
+        _ptr(lse), _stream(stream)))
+
+
+def vsa_kept_stats_ref(prob: Problem, sparsity: float, budget: vsa_ref_budget):
+    kept, frac = ctypes.c_int64(), ctypes.c_double()
+    _check("vsa_kept_stats_ref", lib().vsa_kept_stats_ref(
+        prob.ref, float(sparsity), ctypes.byref(budget), ctypes.byref(kept), ctypes.byref(frac)))
+    return kept.value, frac.value
+
+
+def vsa_count_flops_ref(prob: Problem, sparsity: float, budget: vsa_ref_budget,
+                        slot_to_token_host, kv_idx_host, ref_idx_host):
+    import numpy as np
+    s2t = np.ascontiguousarray(slot_to_token_host, dtype=np.int32)
+    kv = np.ascontiguousarray(kv_idx_host, dtype=np.int32)
+    rf = np.ascontiguousarray(ref_idx_host, dtype=np.int32)
+    out = ctypes.c_double()
+    _check("vsa_count_flops_ref", lib().vsa_count_flops_ref(
+        prob.ref, float(sparsity), ctypes.byref(budget), s2t.ctypes.data, kv.ctypes.data,
+        rf.ctypes.data, ctypes.byref(out)))
+    return out.value
+
+
 # ---------------------------------------------------------- whole-layer helper
 
 class Layer:
@@ -269,7 +370,7 @@ class Layer:
     """
 
     def __init__(self, prob: Problem, sparsity: float, mode: int, proj_dim: int,
-                 device="cuda", with_lse: bool = True):
+                 device="cuda", with_lse: bool = True, ref: Optional[Tuple[int, int]] = None):
         import torch
         self.prob, self.sparsity, self.mode, self.proj_dim = prob, sparsity, mode, proj_dim
         self.sizes = sz = vsa_query_sizes(prob, sparsity)
@@ -285,6 +386,16 @@ class Layer:
         self.out = torch.empty((prob.B, prob.H, prob.N, prob.d), dtype=et, device=dev)
         self.lse = (torch.empty((prob.B, prob.H, prob.N), dtype=torch.float32, device=dev)
                     if with_lse else None)
+        # Two-stream budget (segment, k_ref): buffers of the reference stream.
+        self.budget = None if ref is None else ref_budget(*ref)
+        if self.budget is not None:
+            if sparsity == 0.0:
+                raise ValueError("the two-stream budget needs sparsity > 0")
+            _, se, ie = vsa_ref_sizes(prob, self.budget)
+            rb = vsa_ref_pooled_bytes(prob, mode, proj_dim, self.budget)
+            self.ref_pooled = torch.empty((rb + 7) // 8, dtype=torch.float64, device=dev)
+            self.ref_scores = torch.empty(se, dtype=torch.float32, device=dev)
+            self.ref_idx = torch.empty(ie, dtype=torch.int32, device=dev)
 
     def map_tiles(self, q, k, v, stream=None):
         vsa_map_tiles(self.prob, q, k, v, self.slot_to_token, self.qt, self.kt, self.vt, stream)
@@ -292,12 +403,24 @@ class Layer:
     def tile_scores(self, wq, wk, stream=None):
         vsa_tile_scores(self.prob, self.mode, self.proj_dim, self.qt, self.kt,
                         self.slot_to_token, wq, wk, self.pooled, self.scores, stream)
+        if self.budget is not None:
+            vsa_ref_scores(self.prob, self.mode, self.proj_dim, self.kt, self.slot_to_token, wq,
+                           wk, self.budget, self.pooled, self.ref_pooled, self.ref_scores,
+                           stream)
 
     def select(self, stream=None):
         vsa_select_topk(self.prob, self.scores, self.sparsity, self.kv_idx, stream)
+        if self.budget is not None:
+            vsa_ref_select(self.prob, self.budget, self.ref_scores, self.ref_idx, stream)
 
-    def attend(self, softmax_scale: float = 0.0, stream=None, kv_idx=None):
+    def attend(self, softmax_scale: float = 0.0, stream=None, kv_idx=None, ref_idx=None):
         kv = self.kv_idx if kv_idx is None else kv_idx
+        if self.budget is not None:
+            rf = self.ref_idx if ref_idx is None else ref_idx
+            vsa_sparse_attn_fwd_ref(self.prob, self.qt, self.kt, self.vt, self.slot_to_token, kv,
+                                    self.sparsity, self.budget, rf, softmax_scale, self.out,
+                                    self.lse, stream)
+            return
         vsa_sparse_attn_fwd(self.prob, self.qt, self.kt, self.vt, self.slot_to_token,
                             None if self.sparsity == 0.0 else kv, self.sparsity,
                             softmax_scale, self.out, self.lse, stream)

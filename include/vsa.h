@@ -244,6 +244,83 @@ VSA_API int vsa_count_flops(const vsa_problem *prob, double sparsity,
                             const int32_t *slot_to_token_host,
                             const int32_t *kv_idx_host, double *flops);
 
+/*
+ * Two-stream budget (reference-to-video). One prefix segment, the reference
+ * image, becomes a second sparse stream: its tiles are pooled and scored
+ * against the video query tiles the same way as the video key tiles, and
+ * each video query tile keeps its k_ref best of them (higher score first,
+ * lower tile index first among equal scores). The other prefix segments
+ * stay dense keys and every prefix query row stays dense
+ * ("BSAI-ComfyUI-VedaSparse" README, section "v3.4.2 Vendored Official
+ * Veda (Pull-and-Go)", R2VA predictor row: 32 reference tiles and 32 video
+ * tiles per query, text and audio conditioning dense).
+ */
+typedef struct vsa_ref_budget {
+  int32_t segment;            /* index into prefix_len of the reference segment */
+  int32_t k_ref;              /* reference tiles kept, 1 .. that segment's tiles */
+} vsa_ref_budget;
+
+/*
+ * vsa_ref_sizes - host only: tiles of the reference segment, and the
+ * elements of ref_scores ([B][H][max_video_tiles][n_ref] float) and of
+ * ref_idx ([B][H][max_video_tiles][k_ref] int32).
+ */
+VSA_API int vsa_ref_sizes(const vsa_problem *prob, const vsa_ref_budget *budget,
+                          int32_t *n_ref_tiles, int64_t *ref_score_elems,
+                          int64_t *ref_idx_elems);
+
+/* vsa_ref_pooled_bytes - host only: bytes of ref_pooled_ws (double
+ * [B][H][n_ref][r], r as for vsa_pooled_bytes). */
+VSA_API int vsa_ref_pooled_bytes(const vsa_problem *prob, int32_t mode, int32_t proj_dim,
+                                 const vsa_ref_budget *budget, int64_t *bytes);
+
+/*
+ * vsa_ref_scores - the reference stream's scores. Pools the reference tiles
+ * of kt (wk for TripPool; the gate wk, or wq when wk is NULL, for the mean
+ * gate) into ref_pooled_ws, then ref_scores[b][h][i][j] = the double dot
+ * product of video query tile i's descriptor and reference tile j's,
+ * rounded once to float. pooled_ws must hold the query descriptors written
+ * by vsa_tile_scores with the same mode and proj_dim (it is only read).
+ */
+VSA_API int vsa_ref_scores(const vsa_problem *prob, int32_t mode, int32_t proj_dim,
+                           const void *kt, const int32_t *slot_to_token, const float *wq,
+                           const float *wk, const vsa_ref_budget *budget,
+                           const void *pooled_ws, void *ref_pooled_ws, float *ref_scores,
+                           void *stream);
+
+/*
+ * vsa_ref_select - per video query tile, the k_ref best reference tiles:
+ * ref_idx[b][h][i][0..k_ref) ascending indices into the reference segment's
+ * tiles (0 = its first tile). Same ranking rule as vsa_select_topk.
+ */
+VSA_API int vsa_ref_select(const vsa_problem *prob, const vsa_ref_budget *budget,
+                           const float *ref_scores, int32_t *ref_idx, void *stream);
+
+/*
+ * vsa_sparse_attn_fwd_ref - vsa_sparse_attn_fwd under the two-stream budget:
+ * a video query tile is allowed the non-reference prefix tiles, its ref_idx
+ * reference tiles and its kv_idx video tiles; a prefix query tile is allowed
+ * every tile. sparsity must be > 0. Other arguments as vsa_sparse_attn_fwd.
+ */
+VSA_API int vsa_sparse_attn_fwd_ref(const vsa_problem *prob, const void *qt, const void *kt,
+                                    const void *vt, const int32_t *slot_to_token,
+                                    const int32_t *kv_idx, double sparsity,
+                                    const vsa_ref_budget *budget, const int32_t *ref_idx,
+                                    float softmax_scale, void *out, float *lse,
+                                    void *stream);
+
+/* vsa_kept_stats_ref / vsa_count_flops_ref - host only: as vsa_kept_stats
+ * and vsa_count_flops under the two-stream budget (ref_idx_host: HOST copy
+ * of ref_idx). */
+VSA_API int vsa_kept_stats_ref(const vsa_problem *prob, double sparsity,
+                               const vsa_ref_budget *budget, int64_t *kept_tile_pairs,
+                               double *frac_of_full);
+VSA_API int vsa_count_flops_ref(const vsa_problem *prob, double sparsity,
+                                const vsa_ref_budget *budget,
+                                const int32_t *slot_to_token_host,
+                                const int32_t *kv_idx_host, const int32_t *ref_idx_host,
+                                double *flops);
+
 /* Static text for a vsa_status value. */
 VSA_API const char *vsa_status_string(int status);
 

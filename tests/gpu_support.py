@@ -89,15 +89,16 @@ def problem_of(w: Workload, H=None):
 
 
 def run_library(w: Workload, sparsity=None, stages=("map", "score", "select", "attn"),
-                arrays=None):
-    """Runs the library's layer on the workload's seeded inputs (all heads)."""
+                arrays=None, ref=None):
+    """Runs the library's layer on the workload's seeded inputs (all heads);
+    ``ref`` = (segment, k_ref) turns on the two-stream budget."""
     import torch
     from block_sparse_video_map_amd import vsa
     sp = w.sparsity if sparsity is None else sparsity
     prob = problem_of(w)
     mode = vsa.VSA_SCORE_MEAN_GATE if w.scorer == "mean_gate" else vsa.VSA_SCORE_TRIPPOOL
     proj = w.d if w.scorer == "mean_gate" else w.proj_dim
-    layer = vsa.Layer(prob, sp, mode, proj)
+    layer = vsa.Layer(prob, sp, mode, proj, ref=ref)
     q, k, v = to_device(w, arrays=arrays)
     W = make_weights(w)
     if w.scorer == "mean_gate":
@@ -132,8 +133,10 @@ def head_inputs(w: Workload, h: int, b: int = 0):
 
 
 def oracle_head(w: Workload, h: int, sparsity=None, query_tiles=(), b: int = 0,
-                arrays=None):
-    """The oracle's whole path for one head (attention only on query_tiles)."""
+                arrays=None, ref=None, kv_video=None, kv_ref=None):
+    """The oracle's whole path for one head (attention only on query_tiles);
+    ``ref`` = (segment, k_ref) as for run_library; kv_video / kv_ref replace
+    the oracle's selections (to compare outputs on the GPU's selection)."""
     if arrays is None:
         q, k, v = head_inputs(w, h, b)
     else:
@@ -147,7 +150,8 @@ def oracle_head(w: Workload, h: int, sparsity=None, query_tiles=(), b: int = 0,
     sp = w.sparsity if sparsity is None else sparsity
     qt = None if query_tiles is None else list(query_tiles)
     return oracle.head_forward(q, k, v, w.grid, w.prefix, shape, sp, w.scorer, wq, wk,
-                               query_tiles=qt), (q, k, v)
+                               query_tiles=qt, ref_budget=ref, kv_video=kv_video,
+                               kv_ref=kv_ref), (q, k, v)
 
 
 # ------------------------------------------------------------ comparisons

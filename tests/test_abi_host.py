@@ -193,3 +193,75 @@ def test_pooled_bytes():
     sz = vsa.vsa_query_sizes(p, 0.9)
     assert vsa.vsa_pooled_bytes(p, 1, 32) == sz.pooled_rows * 96 * 8
     assert vsa.vsa_pooled_bytes(p, 0, 128) == sz.pooled_rows * 128 * 8
+
+
+# ------------------------------------------------------------ two-stream budget
+
+def test_ref_budget_struct_layout(tmp_path):
+    src = tmp_path / "ref.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "vsa.h"\n'
+                   'int main(void){printf("%zu %zu\\n", sizeof(vsa_ref_budget),'
+                   ' offsetof(vsa_ref_budget, k_ref)); return 0;}\n')
+    exe = tmp_path / "ref"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert got == [ctypes.sizeof(vsa.vsa_ref_budget), vsa.vsa_ref_budget.k_ref.offset]
+
+
+def test_ref_sizes_follow_the_segment_tiles():
+    w = WORKLOADS["3b"]
+    p = _problem(w)
+    n, se, ie = vsa.vsa_ref_sizes(p, vsa.ref_budget(1, 32))
+    assert n == oracle.segment_tiles(w.prefix, 1).size == 63
+    sz = vsa.vsa_query_sizes(p, w.sparsity)
+    assert se == w.B * w.H * sz.max_video_tiles * 63
+    assert ie == w.B * w.H * sz.max_video_tiles * 32
+    rb = vsa.vsa_ref_pooled_bytes(p, vsa.VSA_SCORE_MEAN_GATE, w.d, vsa.ref_budget(1, 32))
+    assert rb == w.B * w.H * 63 * w.d * 8
+
+
+@pytest.mark.parametrize("segment,k_ref", [(-1, 1), (3, 1), (1, 0), (1, 64), (2, 3)])
+def test_bad_ref_budgets_rejected(segment, k_ref):
+    # 3b: segments of 8, 63 and 2 tiles
+    p = _problem(WORKLOADS["3b"])
+    with pytest.raises(vsa.VSAError) as e:
+        vsa.vsa_ref_sizes(p, vsa.ref_budget(segment, k_ref))
+    assert e.value.status == vsa.VSA_ERR_INVALID_ARG
+
+
+def test_zero_length_reference_segment_rejected():
+    w = WORKLOADS["1"]
+    p = _problem(w, prefix=(40, 0, 24))
+    with pytest.raises(vsa.VSAError):
+        vsa.vsa_ref_sizes(p, vsa.ref_budget(1, 1))
+
+
+def test_ref_kept_stats_and_flops_match_oracle():
+    prefix = (40, 150, 24)
+    w = WORKLOADS["1"]
+    p = _problem(w, prefix=prefix)
+    budget = vsa.ref_budget(1, 2)
+    tm = oracle.tile_map(*w.grid, prefix, w.tile_shapes[0])
+    ref = oracle.segment_tiles(prefix, 1)
+    rng = np.random.default_rng(1)
+    sz = vsa.vsa_query_sizes(p, 0.5)
+    kv = np.full((w.B * w.H, sz.max_video_tiles, sz.k_max), -1, dtype=np.int32)
+    rf = np.zeros((w.B * w.H, sz.max_video_tiles, 2), dtype=np.int32)
+    allows = []
+    for h in range(w.H):
+        sel = np.sort(np.stack([rng.choice(tm.n_video_tiles, sz.k[0], replace=False)
+                                for _ in range(tm.n_video_tiles)]), axis=1)
+        rsel = np.sort(np.stack([rng.choice(ref.size, 2, replace=False)
+                                 for _ in range(tm.n_video_tiles)]), axis=1)
+        kv[h, :, :sz.k[0]] = sel
+        rf[h] = rsel
+        allows.append(oracle.allowed_two_stream(tm, sel, ref, rsel))
+    s2t = tm.slot_to_token.astype(np.int32)
+    got = vsa.vsa_count_flops_ref(p, 0.5, budget, s2t, kv, rf)
+    want = sum(oracle.effective_flops(tm, a, w.d) for a in allows)
+    assert got == want
+    kept, frac = vsa.vsa_kept_stats_ref(p, 0.5, budget)
+    assert kept == sum(int(a.sum()) for a in allows)
+    assert math.isclose(frac, kept / (w.H * tm.n_tiles ** 2), rel_tol=1e-12)
