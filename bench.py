@@ -38,9 +38,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="3a")
-    ap.add_argument("--also", default="3b,3a-h3",
+    ap.add_argument("--also", default="3b,3a-h3,3b-r2va",
                     help="extra workloads reported beside, ',' list; a '-h3' suffix keeps "
-                         "only heads 0-2 (one GPU's share of 24 heads over 8 GPUs)")
+                         "only heads 0-2 (one GPU's share of 24 heads over 8 GPUs); "
+                         "'-r2va' runs the two-stream budget (32 reference tiles of the "
+                         "reference-image segment and 32 video tiles per query tile)")
     ap.add_argument("--dense-steps", type=int, default=2)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -55,7 +57,7 @@ def parse():
 class Case:
     """Library buffers and inputs for one workload, resident on the GPU."""
 
-    def __init__(self, wname: str, sparsity=None, heads=None):
+    def __init__(self, wname: str, sparsity=None, heads=None, ref=None):
         import dataclasses
 
         import numpy as np
@@ -71,7 +73,8 @@ class Case:
         self.prob = vsa.Problem(w.B, w.H, w.d, w.grid, w.prefix, w.tile_shapes, w.dtype)
         mode = vsa.VSA_SCORE_MEAN_GATE if w.scorer == "mean_gate" else vsa.VSA_SCORE_TRIPPOOL
         proj = w.d if w.scorer == "mean_gate" else w.proj_dim
-        self.layer = vsa.Layer(self.prob, self.sparsity, mode, proj, with_lse=False)
+        self.ref = ref
+        self.layer = vsa.Layer(self.prob, self.sparsity, mode, proj, with_lse=False, ref=ref)
         t0 = time.time()
         bits = w.dtype == "bf16"
         q, k, v = make_qkv(w, as_bf16_bits=bits)
@@ -101,6 +104,9 @@ class Case:
         torch.cuda.synchronize()
         s2t = self.layer.slot_to_token.cpu().numpy()
         kv = None if self.sparsity == 0.0 else self.layer.kv_idx.cpu().numpy()
+        if self.ref is not None:
+            return vsa.vsa_count_flops_ref(self.prob, self.sparsity, self.layer.budget, s2t, kv,
+                                           self.layer.ref_idx.cpu().numpy())
         return vsa.vsa_count_flops(self.prob, self.sparsity, s2t, kv)
 
     def time_steps(self, steps: int, warmup: int):
@@ -255,12 +261,13 @@ def main():
 
     extra = {}
     for name in [x for x in a.also.split(",") if x]:
-        heads = None
+        heads, ref, sp, label = None, None, None, name
         if name.endswith("-h3"):          # one GPU's share when 8 GPUs split the heads
             name, heads = name[:-3], 3
-        c = Case(name, heads=heads)
-        if heads is not None:
-            name = f"{name}-h3"
+        if name.endswith("-r2va"):        # two-stream budget: 32 + 32 tiles per query tile
+            name, ref, sp = name[:-5], (1, 32), 0.9819
+        c = Case(name, heads=heads, ref=ref, sparsity=sp)
+        name = label
         f = c.flops()
         ms = c.time_steps(max(3, a.steps // 2), 2) * 1e3
         m2, mn2 = c.stage_times(5)
