@@ -92,6 +92,21 @@ def traffic(fetch_dir: str, write_dir: str, kernel: str, copy_mib: int):
             "per_kernel": per_kernel}
 
 
+def counters(d: str, kernel: str):
+    """Counter totals of the last dispatch of `kernel` in one --pmc run."""
+    rows = list(csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))))
+    acc: dict = {}
+    for r in rows:
+        if kernel not in r["Kernel_Name"]:
+            continue
+        key = (int(r["Dispatch_Id"]), r["Counter_Name"])
+        acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+    if not acc:
+        raise SystemExit(f"kernel {kernel} not found in {d}")
+    last = max(k[0] for k in acc)
+    return {c: v for (i, c), v in sorted(acc.items()) if i == last}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -108,10 +123,23 @@ def main(argv=None):
     t.add_argument("--title", required=True)
     t.add_argument("--command", required=True, help="FETCH_SIZE command; WRITE_SIZE is the same")
     t.add_argument("--workload", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--title", required=True)
+    c.add_argument("--command", required=True)
+    c.add_argument("--note", default="")
     a = ap.parse_args(argv)
     lines = [f"# {a.title}", "", "Command (from the repository root on the GPU host):", "",
              "```", a.command, "```", ""]
-    if a.cmd == "stats":
+    if a.cmd == "counters":
+        if a.note:
+            lines += [a.note, ""]
+        lines += [f"Totals over one dispatch of `{a.kernel}` (all XCDs):", "",
+                  "| counter | value |", "|---|---|"]
+        for k, v in counters(a.dir, a.kernel).items():
+            lines.append(f"| {k} | {v:.4g} |")
+    elif a.cmd == "stats":
         if a.note:
             lines += [a.note, ""]
         lines += ["rocprofv3 `run_kernel_stats.csv`:", ""] + stats_table(a.dir)
