@@ -8,5 +8,5 @@ from .vsa_oracle import (  # noqa: F401
     TILE, TileMap, tile_map, gather, pool_mean_gate, pool_trippool,
     tile_scores, keep_count, select_topk, allowed_tiles, softmax_attention,
     sparse_attention, dense_attention, effective_flops, head_forward,
-    segment_tiles, allowed_two_stream,
+    segment_tiles, allowed_two_stream, teacher_tile_map, tile_recall,
 )

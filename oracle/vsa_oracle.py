@@ -356,6 +356,55 @@ def allowed_two_stream(tmap: TileMap, kv_video, ref_tiles, kv_ref) -> np.ndarray
 
 
 # --------------------------------------------------------------------------
+# 9. Teacher tile map and tile recall
+# --------------------------------------------------------------------------
+
+def teacher_tile_map(q, k, tmap: TileMap, scale: float, query_tiles=None) -> np.ndarray:
+    """Full attention max-pooled per (video query tile, video key tile).
+
+    The teacher distribution at tile level comes from full attention with
+    max pooling ("Veda Sparse Attention в ComfyUI", section "Что делает
+    Veda": the first of the method's three stages). Reading: the attention
+    probability of real query q and real key k is softmax over all real keys
+    (prefix and video) of q.k * scale; the teacher value of a tile pair is the
+    largest such probability over the pair's real queries and keys. Rows are
+    the given video query tiles (default: all), columns all video key tiles.
+    float64 [n_rows, n_video].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    npf = tmap.n_prefix_tiles
+    rows = range(tmap.n_video_tiles) if query_tiles is None else query_tiles
+    keys_all = np.concatenate([tmap.tile_tokens(t) for t in range(tmap.n_tiles)])
+    video_keys = [tmap.tile_tokens(npf + j) for j in range(tmap.n_video_tiles)]
+    out = np.zeros((len(rows), tmap.n_video_tiles))
+    for r, i in enumerate(rows):
+        qs = tmap.tile_tokens(npf + i)
+        logits = (q[qs] @ k[keys_all].T) * scale
+        mx = logits.max(axis=1, keepdims=True)
+        lse = mx + np.log(np.exp(logits - mx).sum(axis=1, keepdims=True))
+        for j, ks in enumerate(video_keys):
+            out[r, j] = np.exp((q[qs] @ k[ks].T) * scale - lse).max()
+    return out
+
+
+def tile_recall(selection, teacher_rows, k: int) -> float:
+    """Share of the teacher's top-k tiles that a selection keeps.
+
+    Tile recall against the max-pooled teacher is the measure the pages use
+    to compare scorers ("BSAI-ComfyUI-VedaSparse" README, Overview table,
+    TripPool row: tile recall of TripPool against mean pooling). Reading: per
+    video query tile, |selection ∩ teacher top-k| / k with the teacher ranked
+    like the scores (higher first, lower index first among ties), averaged
+    over the rows given.
+    """
+    top = select_topk(np.asarray(teacher_rows, dtype=np.float32), k)
+    sel = np.asarray(selection)
+    hits = [len(set(a[:k].tolist()) & set(b.tolist())) for a, b in zip(sel, top)]
+    return float(np.mean(hits)) / k
+
+
+# --------------------------------------------------------------------------
 # The whole path for one (batch, head)
 # --------------------------------------------------------------------------
 

@@ -16,6 +16,7 @@ from tests import test_oracle_attention as ta
 from tests import test_oracle_map as tm_
 from tests import test_oracle_pool_score as tp
 from tests import test_oracle_select as ts
+from tests import test_oracle_teacher as tte
 from tests import test_oracle_two_stream as tts
 
 
@@ -77,6 +78,25 @@ def _segment_tiles_shifted(prefix, segment):
     return _orig_segment_tiles(prefix, segment) + 1
 
 
+def _teacher_max_logit(q, k, tmap, scale, query_tiles=None):
+    # pools the raw logits instead of the attention probabilities
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    npf = tmap.n_prefix_tiles
+    rows = range(tmap.n_video_tiles) if query_tiles is None else query_tiles
+    out = np.zeros((len(rows), tmap.n_video_tiles))
+    for r, i in enumerate(rows):
+        qs = tmap.tile_tokens(npf + i)
+        for j in range(tmap.n_video_tiles):
+            out[r, j] = ((q[qs] @ k[tmap.tile_tokens(npf + j)].T) * scale).max()
+    return out
+
+
+def _recall_over_n(selection, teacher_rows, k):
+    return _orig_recall(selection, teacher_rows, k) * k / np.asarray(teacher_rows).shape[1]
+
+
+_orig_recall = vo.tile_recall
 _orig_two_stream = vo.allowed_two_stream
 _orig_segment_tiles = vo.segment_tiles
 _orig_tile_map = vo.tile_map
@@ -109,6 +129,8 @@ CASES = [
      lambda: ta.test_prefix_rows_are_dense_at_any_sparsity(0.75)),
     ("allowed_two_stream", _two_stream_reference_dense, tts.test_allowed_sets_by_brute_force),
     ("segment_tiles", _segment_tiles_shifted, tts.test_segment_tiles_follow_the_tile_map),
+    ("teacher_tile_map", _teacher_max_logit, tte.test_teacher_map_by_brute_force),
+    ("tile_recall", _recall_over_n, tte.test_tile_recall_hand_cases),
 ]
 
 
