@@ -213,4 +213,18 @@ VSA_API int vsa_sparse_attn_fwd_ref(const vsa_problem *prob, const void *qt, con
                                      lse, (hipStream_t)stream));
 }
 
+VSA_API int vsa_teacher_map(const vsa_problem *prob, const void *qt, const void *kt,
+                            const int32_t *slot_to_token, float softmax_scale, float *lse_ws,
+                            float *teacher, void *stream) {
+  Plan p;
+  int st = make_plan_geometry(prob, &p);
+  if (st != VSA_OK) return st;
+  if (!qt || !kt || !slot_to_token || !lse_ws || !teacher) return VSA_ERR_INVALID_ARG;
+  if (!aligned16(qt) || !aligned16(kt)) return VSA_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale)) return VSA_ERR_INVALID_ARG;
+  float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)p.d);
+  return hip_status(launch_teacher(p, qt, kt, slot_to_token, scale, lse_ws, teacher,
+                                   (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -61,3 +61,7 @@ hipError_t launch_attention(const Plan &p, const void *qt, const void *kt,
                             const void *vt, const int32_t *s2t, const int32_t *kv_idx,
                             const int32_t *ref_idx, float scale, void *out, float *lse,
                             hipStream_t stream);
+// Teacher tile map: two dense passes (per-query log-sum-exp into lse_ws, then
+// the largest attention probability per video tile pair into teacher).
+hipError_t launch_teacher(const Plan &p, const void *qt, const void *kt, const int32_t *s2t,
+                          float scale, float *lse_ws, float *teacher, hipStream_t stream);

@@ -30,7 +30,7 @@ EXPORTS = ("vsa_query_sizes", "vsa_pooled_bytes", "vsa_map_tiles", "vsa_tile_sco
            "vsa_select_topk", "vsa_sparse_attn_fwd", "vsa_kept_stats",
            "vsa_count_flops", "vsa_ref_sizes", "vsa_ref_pooled_bytes", "vsa_ref_scores",
            "vsa_ref_select", "vsa_sparse_attn_fwd_ref", "vsa_kept_stats_ref",
-           "vsa_count_flops_ref", "vsa_status_string", "vsa_version")
+           "vsa_count_flops_ref", "vsa_teacher_map", "vsa_status_string", "vsa_version")
 
 
 class vsa_problem(ctypes.Structure):
@@ -98,6 +98,7 @@ def lib() -> ctypes.CDLL:
             "vsa_sparse_attn_fwd_ref": [P, vp, vp, vp, vp, vp, f64, R, vp, f32, vp, vp, vp],
             "vsa_kept_stats_ref": [P, f64, R, ctypes.POINTER(i64), ctypes.POINTER(f64)],
             "vsa_count_flops_ref": [P, f64, R, vp, vp, vp, ctypes.POINTER(f64)],
+            "vsa_teacher_map": [P, vp, vp, vp, f32, vp, vp, vp],
             "vsa_status_string": [ctypes.c_int],
             "vsa_version": [],
         }
@@ -358,6 +359,22 @@ def vsa_count_flops_ref(prob: Problem, sparsity: float, budget: vsa_ref_budget,
         prob.ref, float(sparsity), ctypes.byref(budget), s2t.ctypes.data, kv.ctypes.data,
         rf.ctypes.data, ctypes.byref(out)))
     return out.value
+
+
+def vsa_teacher_map(prob: Problem, qt, kt, slot_to_token, softmax_scale: float, lse_ws,
+                    teacher, stream=None):
+    """Teacher tile map into ``teacher`` (scores layout); lse_ws holds
+    B*H*max_video_tiles*64 floats."""
+    import torch
+    sz = vsa_query_sizes(prob, 0.0)
+    et = _elem_dtype(prob)
+    for name, x in (("qt", qt), ("kt", kt)):
+        _need(x, sz.tiled_elems, et, name)
+    _need(lse_ws, prob.B * prob.H * sz.max_video_tiles * VSA_TILE, torch.float32, "lse_ws")
+    _need(teacher, sz.score_elems, torch.float32, "teacher")
+    _check("vsa_teacher_map", lib().vsa_teacher_map(
+        prob.ref, _ptr(qt), _ptr(kt), _ptr(slot_to_token), float(softmax_scale), _ptr(lse_ws),
+        _ptr(teacher), _stream(stream)))
 
 
 # ---------------------------------------------------------- whole-layer helper

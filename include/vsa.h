@@ -321,6 +321,21 @@ VSA_API int vsa_count_flops_ref(const vsa_problem *prob, double sparsity,
                                 const int32_t *kv_idx_host, const int32_t *ref_idx_host,
                                 double *flops);
 
+/*
+ * vsa_teacher_map - the teacher tile map, a measurement aid: teacher[b][h][i][j]
+ * is the largest full-attention probability (softmax over all real keys of
+ * q.k * scale) over the real queries of video tile i and the real keys of
+ * video tile j ("Veda Sparse Attention в ComfyUI", section "Что делает Veda":
+ * full attention max-pooled per tile is the teacher). Same layout as the
+ * scores of vsa_tile_scores, so vsa_select_topk on it gives the teacher's
+ * top-k. lse_ws: device float workspace of B*H*max_video_tiles*64 elements
+ * (per-query log-sum-exp, base 2). softmax_scale <= 0 selects 1/sqrt(d).
+ * Costs two dense passes of Q K^T.
+ */
+VSA_API int vsa_teacher_map(const vsa_problem *prob, const void *qt, const void *kt,
+                            const int32_t *slot_to_token, float softmax_scale, float *lse_ws,
+                            float *teacher, void *stream);
+
 /* Static text for a vsa_status value. */
 VSA_API const char *vsa_status_string(int status);
 
