@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--dense-steps", type=int, default=2)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-recall", action="store_true",
+                    help="skip the teacher tile-map recall measurement")
     ap.add_argument("--profile-attn-only", action="store_true",
                     help="run only warmup+steps of the layer (for profilers)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -57,7 +59,8 @@ def parse():
 class Case:
     """Library buffers and inputs for one workload, resident on the GPU."""
 
-    def __init__(self, wname: str, sparsity=None, heads=None, ref=None):
+    def __init__(self, wname: str, sparsity=None, heads=None, ref=None, workload=None,
+                 inputs=None):
         import dataclasses
 
         import numpy as np
@@ -65,7 +68,7 @@ class Case:
         from block_sparse_video_map_amd import vsa
         from workloads import WORKLOADS
         from workloads.inputs import make_qkv, make_weights
-        w = WORKLOADS[wname]
+        w = WORKLOADS[wname] if workload is None else workload
         if heads is not None:
             w = dataclasses.replace(w, H=heads)
         self.w = w
@@ -77,12 +80,15 @@ class Case:
         self.layer = vsa.Layer(self.prob, self.sparsity, mode, proj, with_lse=False, ref=ref)
         t0 = time.time()
         bits = w.dtype == "bf16"
-        q, k, v = make_qkv(w, as_bf16_bits=bits)
-        dev = [torch.from_numpy(x).cuda() for x in (q, k, v)]
-        del q, k, v
-        if bits:
-            dev = [x.view(torch.bfloat16) for x in dev]
-        self.q, self.k, self.v = dev
+        if inputs is not None:                     # device tensors of another case
+            self.q, self.k, self.v = inputs
+        else:
+            q, k, v = make_qkv(w, as_bf16_bits=bits)
+            dev = [torch.from_numpy(x).cuda() for x in (q, k, v)]
+            del q, k, v
+            if bits:
+                dev = [x.view(torch.bfloat16) for x in dev]
+            self.q, self.k, self.v = dev
         W = make_weights(w)
         if w.scorer == "mean_gate":
             self.wq, self.wk = torch.from_numpy(W["gate"]).cuda(), None
@@ -166,6 +172,57 @@ class Case:
         import torch
         del self.layer, self.q, self.k, self.v
         torch.cuda.empty_cache()
+
+
+def teacher_recall(wname: str):
+    """Tile recall of the mean-gate and the TripPool selections against the
+    teacher tile map (full attention max-pooled per tile pair), both at the
+    workload's sparsity on the same synthetic inputs. A measurement: random
+    untrained gates and projections, so the values are not the pages'."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+    from block_sparse_video_map_amd import vsa
+    from workloads import WORKLOADS
+    w = WORKLOADS[wname]
+    other = "trippool" if w.scorer == "mean_gate" else "mean_gate"
+    base = Case(wname)
+    alt = Case(wname, workload=dataclasses.replace(w, scorer=other),
+               inputs=(base.q, base.k, base.v))
+    sels = {w.scorer: base, other: alt}
+    for c in sels.values():
+        c.step()
+    sz = base.layer.sizes
+    lse = torch.empty(w.B * w.H * sz.max_video_tiles * 64, dtype=torch.float32, device="cuda")
+    teacher = torch.empty(sz.score_elems, dtype=torch.float32, device="cuda")
+    top = torch.empty(sz.idx_elems, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    vsa.vsa_teacher_map(base.prob, base.layer.qt, base.layer.kt, base.layer.slot_to_token, 0.0,
+                        lse, teacher)
+    torch.cuda.synchronize()
+    t_ms = (time.perf_counter() - t0) * 1e3
+    vsa.vsa_select_topk(base.prob, teacher, base.sparsity, top)
+    shp = (w.B * w.H, sz.max_video_tiles, sz.k_max)
+    top = top.view(*shp).cpu().numpy()
+    out = {}
+    for name, c in sels.items():
+        sel = c.layer.kv_idx[: sz.idx_elems].view(*shp).cpu().numpy()
+        rec = []
+        for bh in range(w.B * w.H):
+            s = bh % w.H % len(w.tile_shapes)
+            n, k = sz.n_video_tiles[s], sz.k[s]
+            a, t = np.sort(sel[bh, :n, :k], axis=1), np.sort(top[bh, :n, :k], axis=1)
+            hits = [np.intersect1d(x, y, assume_unique=True).size for x, y in zip(a, t)]
+            rec.append(float(np.mean(hits)) / k)
+        out[name] = round(float(np.mean(rec)), 4)
+    alt.release()
+    base.release()
+    out["teacher_map_ms"] = round(t_ms, 2)
+    out["note"] = ("synthetic inputs, untrained gates/projections: a measurement of the "
+                   "pipeline, not comparable to trained predictors")
+    return out
 
 
 def cpu_baseline(wname: str, budget_s: float):
@@ -278,6 +335,12 @@ def main():
         c.release()
         log(f"[bench] {name}: {ms:.3f} ms/step")
 
+    recall = None
+    if not a.no_recall:
+        log("[bench] teacher tile-map recall")
+        recall = teacher_recall(a.workload)
+        log(f"[bench] recall {recall}")
+
     cpu = None
     if not a.no_cpu_baseline:
         log("[bench] cpu baseline (oracle, bounded sample)")
@@ -323,6 +386,7 @@ def main():
                   "effective_tflops_attention": dense_flops / dmean["attention"] / 1e9},
         "speedup_vs_dense_layer": round(dense_ms / ms_step, 3),
         "also": extra,
+        "teacher_recall": recall,
     }
     print(json.dumps(line), flush=True)
 
