@@ -154,7 +154,11 @@ def pool_mean_gate(xt: np.ndarray, tmap: TileMap, gate: np.ndarray, tiles=None) 
     return mean @ np.asarray(gate, dtype=np.float64)
 
 
-def pool_trippool(xt: np.ndarray, tmap: TileMap, proj: np.ndarray, tiles=None) -> np.ndarray:
+TRIPOOL_MODES = ("triplet", "maxmin", "avg")
+
+
+def pool_trippool(xt: np.ndarray, tmap: TileMap, proj: np.ndarray, tiles=None,
+                  stats: str = "triplet") -> np.ndarray:
     """Veda TripPool tile descriptor: [Avg, Max, Min] of projected tokens.
 
     Each real token of a video tile is projected by the head's d x r matrix,
@@ -162,9 +166,16 @@ def pool_trippool(xt: np.ndarray, tmap: TileMap, proj: np.ndarray, tiles=None) -
     tokens are concatenated ("BSAI-ComfyUI-VedaSparse" README, Overview table,
     TripPool row: Avg, Max and Min statistics per tile; Implementation
     section, the TripPool descriptor). Reading: project first, pool after;
-    pads are left out. ``tiles`` as for pool_mean_gate. Returns float64
-    [n_tiles, 3r].
+    pads are left out. ``tiles`` as for pool_mean_gate.
+
+    ``stats`` is the README's tripool_mode parameter (parameter table:
+    triplet, the default and the paper's best, or maxmin, or avg). Reading:
+    maxmin keeps the [Max, Min] blocks and avg the [Avg] block, in the
+    triplet's order. Returns float64 [n_tiles, 3r], [n_tiles, 2r] or
+    [n_tiles, r].
     """
+    if stats not in TRIPOOL_MODES:
+        raise ValueError(f"unknown tripool mode {stats!r}")
     x, v = _tiles_part(xt, tmap, tiles)
     y = x @ np.asarray(proj, dtype=np.float64)            # [n_video, 64, r]
     counts = v.sum(axis=1).astype(np.float64)
@@ -172,7 +183,8 @@ def pool_trippool(xt: np.ndarray, tmap: TileMap, proj: np.ndarray, tiles=None) -
     avg = np.where(m, y, 0.0).sum(axis=1) / counts[:, None]
     mx = np.where(m, y, -np.inf).max(axis=1)
     mn = np.where(m, y, np.inf).min(axis=1)
-    return np.concatenate([avg, mx, mn], axis=1)
+    blocks = {"triplet": [avg, mx, mn], "maxmin": [mx, mn], "avg": [avg]}[stats]
+    return np.concatenate(blocks, axis=1)
 
 
 # --------------------------------------------------------------------------
@@ -410,11 +422,12 @@ def tile_recall(selection, teacher_rows, k: int) -> float:
 
 def head_forward(q, k, v, grid, prefix, shape, sparsity, scorer, wq, wk=None,
                  scale=None, query_tiles=None, kv_video=None, ref_budget=None,
-                 kv_ref=None):
+                 kv_ref=None, tripool_mode="triplet"):
     """Map -> gather -> pool -> score -> select -> attention for one head.
 
     ``scorer`` is "mean_gate" (``wq`` is the gate; ``wk`` defaults to it) or
-    "trippool" (``wq``, ``wk`` are the per-head projections). ``kv_video``
+    "trippool" (``wq``, ``wk`` are the per-head projections; ``tripool_mode``
+    picks the statistics, see pool_trippool). ``kv_video``
     overrides the selection (a caller-supplied valid selection).
     ``ref_budget`` = (segment, k_ref) turns on the two-stream budget: that
     prefix segment's tiles are scored and k_ref of them kept per video query
@@ -427,7 +440,11 @@ def head_forward(q, k, v, grid, prefix, shape, sparsity, scorer, wq, wk=None,
     tmap = tile_map(T, Hv, Wv, prefix, shape)
     qt, kt = gather(q, tmap), gather(k, tmap)
     wk = wq if wk is None else wk
-    pool = pool_mean_gate if scorer == "mean_gate" else pool_trippool
+    if scorer == "mean_gate":
+        pool = pool_mean_gate
+    else:
+        def pool(xt, tm, w, tiles=None):
+            return pool_trippool(xt, tm, w, tiles, stats=tripool_mode)
     qhat, khat = pool(qt, tmap, wq), pool(kt, tmap, wk)
     scores = tile_scores(qhat, khat)
     kk = keep_count(sparsity, tmap.n_video_tiles)

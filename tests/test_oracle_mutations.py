@@ -34,10 +34,25 @@ def _pool_mean_with_pads(xt, tmap, gate, tiles=None):
     return x.mean(axis=1) @ np.asarray(gate, dtype=np.float64)
 
 
-def _trippool_wrong_order(xt, tmap, proj, tiles=None):
+def _trippool_wrong_order(xt, tmap, proj, tiles=None, stats="triplet"):
     r = np.asarray(proj).shape[1]
-    p = _orig_trippool(xt, tmap, proj, tiles)
+    p = _orig_trippool(xt, tmap, proj, tiles, stats)
     return np.concatenate([p[:, r:2 * r], p[:, :r], p[:, 2 * r:]], axis=1)
+
+
+def _trippool_maxmin_swapped(xt, tmap, proj, tiles=None, stats="triplet"):
+    p = _orig_trippool(xt, tmap, proj, tiles, stats)
+    if stats != "maxmin":
+        return p
+    r = np.asarray(proj).shape[1]
+    return np.concatenate([p[:, r:], p[:, :r]], axis=1)   # [Min | Max]
+
+
+def _trippool_avg_with_pads(xt, tmap, proj, tiles=None, stats="triplet"):
+    if stats != "avg":
+        return _orig_trippool(xt, tmap, proj, tiles, stats)
+    x, _ = vo._tiles_part(xt, tmap, tiles)
+    return (x @ np.asarray(proj, dtype=np.float64)).mean(axis=1)   # pads counted
 
 
 def _scores_transposed(qhat, khat):
@@ -121,6 +136,8 @@ CASES = [
     ("tile_map", _map_prefix_shared, _run_prefix_pin),
     ("pool_mean_gate", _pool_mean_with_pads, tp.test_mean_gate_constant_tile_closed_form),
     ("pool_trippool", _trippool_wrong_order, tp.test_trippool_order_and_values_by_hand),
+    ("pool_trippool", _trippool_maxmin_swapped, tp.test_tripool_modes_by_hand),
+    ("pool_trippool", _trippool_avg_with_pads, tp.test_tripool_avg_is_the_projected_mean_gate),
     ("tile_scores", _scores_transposed, tp.test_scores_direct_formula_and_orientation),
     ("select_topk", _select_high_index_ties, ts.test_ties_go_to_lower_index_and_signed_zero_ties),
     ("keep_count", _keep_count_float_ceil, ts.test_keep_count_exact_where_float_ceil_is_not),

@@ -1,5 +1,6 @@
 """Pins for the oracle's tile pooling and scoring (CPU only)."""
 import numpy as np
+import pytest
 
 import oracle
 
@@ -45,6 +46,48 @@ def test_trippool_order_and_values_by_hand():
     got = oracle.pool_trippool(oracle.gather(x, tm), tm, proj)
     # [avg(c0), avg(c1), max(c0), max(c1), min(c0), min(c1)]
     np.testing.assert_allclose(got[0], [3.0, 0.5, 6.0, 5.0, 1.0, -4.0], rtol=0, atol=1e-15)
+
+
+def test_tripool_modes_by_hand():
+    # tripool_mode maxmin keeps [Max | Min], avg keeps [Avg]; same tile as above
+    tm = oracle.tile_map(1, 1, 3, (), (4, 4, 4))
+    x = np.array([[1.0, -4.0, 9.0], [2.0, 5.0, 9.0], [6.0, 0.5, 9.0]])
+    proj = np.array([[1.0, 0.0], [0.0, 1.0], [0.0, 0.0]])
+    xt = oracle.gather(x, tm)
+    mm = oracle.pool_trippool(xt, tm, proj, stats="maxmin")
+    av = oracle.pool_trippool(xt, tm, proj, stats="avg")
+    np.testing.assert_allclose(mm[0], [6.0, 5.0, 1.0, -4.0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(av[0], [3.0, 0.5], rtol=0, atol=1e-15)
+    with pytest.raises(ValueError):
+        oracle.pool_trippool(xt, tm, proj, stats="minmax")
+
+
+def test_tripool_avg_is_the_projected_mean_gate():
+    # Avg of projected tokens = (mean of tokens) x projection: the mean-gate
+    # descriptor with the projection as the gate (linearity of the mean);
+    # ragged grid, so edge tiles hold pads
+    tm, x, xt = _tiles((5, 6, 7), (40, 64, 24), (4, 4, 4), 16)
+    assert not tm.valid()[tm.n_prefix_tiles:].all()
+    proj = np.random.default_rng(6).standard_normal((16, 16))
+    np.testing.assert_allclose(oracle.pool_trippool(xt, tm, proj, stats="avg"),
+                               oracle.pool_mean_gate(xt, tm, proj), rtol=1e-12, atol=1e-12)
+
+
+def test_tripool_maxmin_constant_tiles_score_is_twice_mean_gate_score():
+    d, r = 8, 5
+    tm = oracle.tile_map(8, 8, 8, (), (4, 4, 4))
+    rng = np.random.default_rng(7)
+    consts = rng.standard_normal((tm.n_video_tiles, d))
+    x = np.zeros((512, d))
+    for i in range(tm.n_video_tiles):
+        x[tm.tile_tokens(i)] = consts[i]
+    xt = oracle.gather(x, tm)
+    pq, pk = rng.standard_normal((d, r)), rng.standard_normal((d, r))
+    mm = oracle.tile_scores(oracle.pool_trippool(xt, tm, pq, stats="maxmin"),
+                            oracle.pool_trippool(xt, tm, pk, stats="maxmin"))
+    mean = oracle.tile_scores(oracle.pool_mean_gate(xt, tm, pq),
+                              oracle.pool_mean_gate(xt, tm, pk))
+    np.testing.assert_allclose(mm, 2.0 * mean, rtol=2e-7)
 
 
 def test_trippool_max_ge_avg_ge_min_and_pads_excluded():
