@@ -74,7 +74,7 @@ class Case:
         self.w = w
         self.sparsity = w.sparsity if sparsity is None else sparsity
         self.prob = vsa.Problem(w.B, w.H, w.d, w.grid, w.prefix, w.tile_shapes, w.dtype)
-        mode = vsa.VSA_SCORE_MEAN_GATE if w.scorer == "mean_gate" else vsa.VSA_SCORE_TRIPPOOL
+        mode = vsa.score_mode(w.scorer, w.tripool_mode)
         proj = w.d if w.scorer == "mean_gate" else w.proj_dim
         self.ref = ref
         self.layer = vsa.Layer(self.prob, self.sparsity, mode, proj, with_lse=False, ref=ref)
@@ -161,7 +161,8 @@ class Case:
         vt = sum(sz.n_video_tiles[s] for s in heads) * w.B
         vt2 = sum(sz.n_video_tiles[s] ** 2 for s in heads) * w.B
         kk = sum(sz.n_video_tiles[s] * sz.k[s] for s in heads) * w.B
-        r = w.d if w.scorer == "mean_gate" else 3 * w.proj_dim
+        nstat = {"triplet": 3, "maxmin": 2, "avg": 1}[w.tripool_mode]
+        r = w.d if w.scorer == "mean_gate" else nstat * w.proj_dim
         out = {"map_gather": 3 * es * w.B * w.H * w.N * w.d + 3 * es * tiles * 64 * w.d}
         if self.sparsity != 0.0:
             out["scores"] = 2 * es * vt * 64 * w.d + 2 * 8 * vt * r + 4 * vt2
@@ -244,7 +245,7 @@ def cpu_baseline(wname: str, budget_s: float):
     wk = None if w.scorer == "mean_gate" else W["proj_k"][0]
     t0 = time.perf_counter()
     r = oracle.head_forward(q, k, v, w.grid, w.prefix, shape, w.sparsity, w.scorer, wq, wk,
-                            query_tiles=[])
+                            query_tiles=[], tripool_mode=w.tripool_mode)
     tm, allow = r["tmap"], r["allow"]
     order = list(range(tm.n_prefix_tiles)) + list(
         np.random.default_rng(0).permutation(np.arange(tm.n_prefix_tiles, tm.n_tiles)))

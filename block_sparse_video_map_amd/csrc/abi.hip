@@ -63,7 +63,7 @@ VSA_API int vsa_tile_scores(const vsa_problem *prob, int32_t mode, int32_t proj_
   st = vsa_pooled_bytes(prob, mode, proj_dim, &bytes);
   if (st != VSA_OK) return st;
   if (!qt || !kt || !slot_to_token || !wq || !pooled_ws || !scores) return VSA_ERR_INVALID_ARG;
-  if (mode == VSA_SCORE_TRIPPOOL && !wk) return VSA_ERR_INVALID_ARG;
+  if (mode != VSA_SCORE_MEAN_GATE && !wk) return VSA_ERR_INVALID_ARG;
   if (!aligned16(qt) || !aligned16(kt) || ((uintptr_t)pooled_ws & 7u))
     return VSA_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
@@ -77,7 +77,8 @@ VSA_API int vsa_tile_scores(const vsa_problem *prob, int32_t mode, int32_t proj_
   job.w[1] = (mode == VSA_SCORE_MEAN_GATE && !wk) ? wq : wk;
   hipError_t e = launch_pool(p, mode, proj_dim, job, 2, slot_to_token, (double *)pooled_ws, s);
   if (e != hipSuccess) return VSA_ERR_HIP;
-  const int r = mode == VSA_SCORE_MEAN_GATE ? p.d : 3 * proj_dim;
+  int r = 0;
+  descriptor_width(mode, proj_dim, p.d, &r);         // validated by vsa_pooled_bytes
   const int64_t bh = (int64_t)p.B * p.H;
   ScoreJob sj;
   sj.q = (const double *)pooled_ws;
@@ -143,7 +144,7 @@ VSA_API int vsa_ref_scores(const vsa_problem *prob, int32_t mode, int32_t proj_d
   if (st != VSA_OK) return st;
   if (!kt || !slot_to_token || !wq || !pooled_ws || !ref_pooled_ws || !ref_scores)
     return VSA_ERR_INVALID_ARG;
-  if (mode == VSA_SCORE_TRIPPOOL && !wk) return VSA_ERR_INVALID_ARG;
+  if (mode != VSA_SCORE_MEAN_GATE && !wk) return VSA_ERR_INVALID_ARG;
   if (!aligned16(kt) || ((uintptr_t)pooled_ws & 7u) || ((uintptr_t)ref_pooled_ws & 7u))
     return VSA_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
@@ -157,7 +158,8 @@ VSA_API int vsa_ref_scores(const vsa_problem *prob, int32_t mode, int32_t proj_d
   hipError_t e = launch_pool(p, mode, proj_dim, job, 1, slot_to_token,
                              (double *)ref_pooled_ws, s);
   if (e != hipSuccess) return VSA_ERR_HIP;
-  const int r = mode == VSA_SCORE_MEAN_GATE ? p.d : 3 * proj_dim;
+  int r = 0;
+  descriptor_width(mode, proj_dim, p.d, &r);         // validated by vsa_pooled_bytes
   ScoreJob sj;
   sj.q = (const double *)pooled_ws;                  // video query descriptors
   sj.q_bh = (int64_t)p.max_vt * r;

@@ -96,6 +96,20 @@ int make_plan(const vsa_problem *prob, double sparsity, Plan *p) {
   return VSA_OK;
 }
 
+int descriptor_width(int mode, int proj_dim, int d, int *r) {
+  if (mode == VSA_SCORE_MEAN_GATE) {
+    if (proj_dim != d) return VSA_ERR_INVALID_ARG;
+    *r = d;
+    return VSA_OK;
+  }
+  const int stats = trippool_stats(mode);
+  if (!stats) return VSA_ERR_INVALID_ARG;
+  if (proj_dim < 8 || proj_dim > VSA_MAX_PROJ || (proj_dim & (proj_dim - 1)))
+    return VSA_ERR_UNSUPPORTED;
+  *r = proj_dim * __builtin_popcount(stats);
+  return VSA_OK;
+}
+
 int apply_ref_budget(const vsa_ref_budget *rb, Plan *p) {
   if (!rb) return VSA_ERR_INVALID_ARG;
   if (rb->segment < 0 || rb->segment >= p->n_prefix) return VSA_ERR_INVALID_ARG;
@@ -143,17 +157,9 @@ VSA_API int vsa_pooled_bytes(const vsa_problem *prob, int32_t mode, int32_t proj
   Plan p;
   int st = make_plan_geometry(prob, &p);
   if (st != VSA_OK) return st;
-  int64_t r;
-  if (mode == VSA_SCORE_MEAN_GATE) {
-    if (proj_dim != p.d) return VSA_ERR_INVALID_ARG;
-    r = p.d;
-  } else if (mode == VSA_SCORE_TRIPPOOL) {
-    if (proj_dim < 8 || proj_dim > VSA_MAX_PROJ || (proj_dim & (proj_dim - 1)))
-      return VSA_ERR_UNSUPPORTED;
-    r = 3 * (int64_t)proj_dim;
-  } else {
-    return VSA_ERR_INVALID_ARG;
-  }
+  int r = 0;
+  st = descriptor_width(mode, proj_dim, p.d, &r);
+  if (st != VSA_OK) return st;
   *bytes = 2 * (int64_t)p.B * p.H * p.max_vt * r * (int64_t)sizeof(double);
   return VSA_OK;
 }

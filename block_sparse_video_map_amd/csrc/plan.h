@@ -40,3 +40,19 @@ int make_plan_geometry(const vsa_problem *prob, Plan *plan);
 
 // Validates a two-stream budget against the plan and records it there.
 int apply_ref_budget(const vsa_ref_budget *budget, Plan *plan);
+
+// Width r (doubles) of one tile descriptor for a score mode. Returns a
+// vsa_status: mean gate needs proj_dim == d; the TripPool modes a power of
+// two in 8..VSA_MAX_PROJ, r = proj_dim times the number of statistics.
+int descriptor_width(int mode, int proj_dim, int d, int *r);
+
+// TripPool statistics a mode writes, as bits: 1 Avg, 2 Max, 4 Min (blocks
+// in that order); 0 for the mean gate.
+inline int trippool_stats(int mode) {
+  switch (mode) {
+    case VSA_SCORE_TRIPPOOL: return 7;
+    case VSA_SCORE_TRIPPOOL_MAXMIN: return 6;
+    case VSA_SCORE_TRIPPOOL_AVG: return 1;
+    default: return 0;
+  }
+}

@@ -146,7 +146,8 @@ __global__ __launch_bounds__(256) void pool_mean_gate_kernel(
   }
 }
 
-// Veda TripPool: project every real token (d -> R), then [Avg | Max | Min].
+// Veda TripPool: project every real token (d -> R), then the statistics the
+// mode asks for, written in the order [Avg | Max | Min] (bits 1, 2, 4 of stats).
 // The projection X[64 tokens x D] . P[D x R] runs on the 16x16x4 f64 MFMA:
 // wave w owns tokens 16w..16w+15 and all R columns (16-column blocks). Lane
 // l reads four consecutive channels k0 + 4*(l/16) + m of its token row and of
@@ -155,7 +156,8 @@ __global__ __launch_bounds__(256) void pool_mean_gate_kernel(
 // (l % 16); the statistics are reduced across lanes, then across waves.
 template <typename T, int D, int R>
 __global__ __launch_bounds__(256) void pool_trippool_kernel(
-    Plan p, PoolJob job, const int32_t *__restrict__ s2t, double *__restrict__ pooled) {
+    Plan p, PoolJob job, int stats, const int32_t *__restrict__ s2t,
+    double *__restrict__ pooled) {
   constexpr int LD = D + 4;                  // float rows, 16-byte aligned
   constexpr int RB = (R + 15) / 16;          // 16-column blocks
   __shared__ __attribute__((aligned(16))) float xs[kTile * LD];
@@ -240,10 +242,17 @@ __global__ __launch_bounds__(256) void pool_trippool_kernel(
       tx = fmax(tx, red[1][ww][j]);
       tn = fmin(tn, red[2][ww][j]);
     }
-    double *out = pooled + (((int64_t)which * p.B * p.H + bh) * job.rows + vt_i) * (3 * R);
-    out[j] = ts / (double)n;
-    out[R + j] = tx;
-    out[2 * R + j] = tn;
+    const int width = __builtin_popcount(stats) * R;
+    double *out = pooled + (((int64_t)which * p.B * p.H + bh) * job.rows + vt_i) * width + j;
+    if (stats & 1) {
+      *out = ts / (double)n;
+      out += R;
+    }
+    if (stats & 2) {
+      *out = tx;
+      out += R;
+    }
+    if (stats & 4) *out = tn;
   }
 }
 
@@ -357,7 +366,7 @@ hipError_t pool_t(const Plan &p, int mode, int R, const PoolJob &job, int nsrc,
 #define VSA_TRIP(RR)                                                                    \
   case RR:                                                                              \
     hipLaunchKernelGGL((pool_trippool_kernel<T, D, RR>), grid, dim3(256), 0, st, p, job, \
-                       s2t, pooled);                                                     \
+                       trippool_stats(mode), s2t, pooled);                               \
     break;
       VSA_TRIP(8) VSA_TRIP(16) VSA_TRIP(32) VSA_TRIP(64)
 #undef VSA_TRIP

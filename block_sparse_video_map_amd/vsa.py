@@ -22,6 +22,7 @@ LIB_PATH = os.environ.get("VSA_LIBRARY") or os.path.join(_PKG, "libvsa.so")
 VSA_OK, VSA_ERR_INVALID_ARG, VSA_ERR_UNSUPPORTED, VSA_ERR_SIZE, VSA_ERR_HIP = 0, -1, -2, -3, -4
 VSA_F32, VSA_BF16 = 0, 1
 VSA_SCORE_MEAN_GATE, VSA_SCORE_TRIPPOOL = 0, 1
+VSA_SCORE_TRIPPOOL_MAXMIN, VSA_SCORE_TRIPPOOL_AVG = 2, 3
 VSA_TILE, VSA_MAX_SEGMENTS, VSA_MAX_SHAPES = 64, 8, 16
 VSA_MAX_VIDEO_TILES, VSA_MAX_PROJ = 8192, 64
 
@@ -159,6 +160,20 @@ class Problem:
     @property
     def ref(self):
         return ctypes.byref(self._struct)
+
+
+def score_mode(scorer: str, tripool_mode: str = "triplet") -> int:
+    """vsa_score_mode for a scorer name ("mean_gate" or "trippool") and, for
+    TripPool, the statistics kept ("triplet", "maxmin" or "avg")."""
+    if scorer == "mean_gate":
+        return VSA_SCORE_MEAN_GATE
+    if scorer != "trippool":
+        raise ValueError(f"unknown scorer {scorer!r}")
+    modes = {"triplet": VSA_SCORE_TRIPPOOL, "maxmin": VSA_SCORE_TRIPPOOL_MAXMIN,
+             "avg": VSA_SCORE_TRIPPOOL_AVG}
+    if tripool_mode not in modes:
+        raise ValueError(f"unknown tripool mode {tripool_mode!r}")
+    return modes[tripool_mode]
 
 
 def vsa_query_sizes(prob: Problem, sparsity: float) -> vsa_sizes:

@@ -65,7 +65,9 @@ typedef enum vsa_dtype { VSA_F32 = 0, VSA_BF16 = 1 } vsa_dtype;
 
 typedef enum vsa_score_mode {
   VSA_SCORE_MEAN_GATE = 0,    /* VSA: mean-pool, then the per-head gate */
-  VSA_SCORE_TRIPPOOL = 1      /* Veda: project tokens, then Avg|Max|Min */
+  VSA_SCORE_TRIPPOOL = 1,     /* Veda: project tokens, then Avg|Max|Min */
+  VSA_SCORE_TRIPPOOL_MAXMIN = 2,  /* Veda tripool_mode maxmin: Max|Min */
+  VSA_SCORE_TRIPPOOL_AVG = 3      /* Veda tripool_mode avg: Avg */
 } vsa_score_mode;
 
 /* One attention layer's geometry. */
@@ -169,6 +171,10 @@ VSA_API int vsa_map_tiles(const vsa_problem *prob, const void *q,
  *   the tile's real tokens (TripPool: "BSAI-ComfyUI-VedaSparse" README,
  *   Overview table). wq, wk: float [H][d][proj_dim]; proj_dim a power of two
  *   in 8..VSA_MAX_PROJ.
+ * modes VSA_SCORE_TRIPPOOL_MAXMIN / _AVG: the same projection, keeping only
+ *   the [Max | Min] or the [Avg] blocks (the README's tripool_mode parameter,
+ *   parameter table: triplet, maxmin, avg). Descriptor width is 3, 2 or 1
+ *   times proj_dim.
  * Pads never enter a descriptor. Descriptors are accumulated in double.
  *
  * scores: float [B][H][max_video_tiles][max_video_tiles], row = video query

@@ -96,7 +96,7 @@ def run_library(w: Workload, sparsity=None, stages=("map", "score", "select", "a
     from block_sparse_video_map_amd import vsa
     sp = w.sparsity if sparsity is None else sparsity
     prob = problem_of(w)
-    mode = vsa.VSA_SCORE_MEAN_GATE if w.scorer == "mean_gate" else vsa.VSA_SCORE_TRIPPOOL
+    mode = vsa.score_mode(w.scorer, w.tripool_mode)
     proj = w.d if w.scorer == "mean_gate" else w.proj_dim
     layer = vsa.Layer(prob, sp, mode, proj, ref=ref)
     q, k, v = to_device(w, arrays=arrays)
@@ -151,7 +151,7 @@ def oracle_head(w: Workload, h: int, sparsity=None, query_tiles=(), b: int = 0,
     qt = None if query_tiles is None else list(query_tiles)
     return oracle.head_forward(q, k, v, w.grid, w.prefix, shape, sp, w.scorer, wq, wk,
                                query_tiles=qt, ref_budget=ref, kv_video=kv_video,
-                               kv_ref=kv_ref), (q, k, v)
+                               kv_ref=kv_ref, tripool_mode=w.tripool_mode), (q, k, v)
 
 
 # ------------------------------------------------------------ comparisons

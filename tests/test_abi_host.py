@@ -193,6 +193,30 @@ def test_pooled_bytes():
     sz = vsa.vsa_query_sizes(p, 0.9)
     assert vsa.vsa_pooled_bytes(p, 1, 32) == sz.pooled_rows * 96 * 8
     assert vsa.vsa_pooled_bytes(p, 0, 128) == sz.pooled_rows * 128 * 8
+    # tripool_mode maxmin and avg keep two and one statistics
+    assert vsa.vsa_pooled_bytes(p, vsa.VSA_SCORE_TRIPPOOL_MAXMIN, 32) == sz.pooled_rows * 64 * 8
+    assert vsa.vsa_pooled_bytes(p, vsa.VSA_SCORE_TRIPPOOL_AVG, 16) == sz.pooled_rows * 16 * 8
+    for mode in (1, 2, 3):
+        for bad in (4, 12, 128):
+            with pytest.raises(vsa.VSAError) as e:
+                vsa.vsa_pooled_bytes(p, mode, bad)
+            assert e.value.status == vsa.VSA_ERR_UNSUPPORTED
+    with pytest.raises(vsa.VSAError) as e:
+        vsa.vsa_pooled_bytes(p, 4, 32)
+    assert e.value.status == vsa.VSA_ERR_INVALID_ARG
+    rb = vsa.ref_budget(1, 8)
+    assert (vsa.vsa_ref_pooled_bytes(p, vsa.VSA_SCORE_TRIPPOOL_MAXMIN, 32, rb)
+            == 2 * vsa.vsa_ref_pooled_bytes(p, vsa.VSA_SCORE_TRIPPOOL_AVG, 32, rb))
+
+
+def test_score_mode_names():
+    assert vsa.score_mode("mean_gate") == vsa.VSA_SCORE_MEAN_GATE
+    assert vsa.score_mode("trippool") == vsa.VSA_SCORE_TRIPPOOL
+    assert vsa.score_mode("trippool", "maxmin") == vsa.VSA_SCORE_TRIPPOOL_MAXMIN
+    assert vsa.score_mode("trippool", "avg") == vsa.VSA_SCORE_TRIPPOOL_AVG
+    for bad in (("trippool", "minmax"), ("gate", "triplet")):
+        with pytest.raises(ValueError):
+            vsa.score_mode(*bad)
 
 
 # ------------------------------------------------------------ two-stream budget

@@ -41,6 +41,7 @@ class Workload:
     sparsity: float
     seed: int
     proj_dim: int = 32              # TripPool per-head projection width
+    tripool_mode: str = "triplet"   # TripPool statistics: triplet, maxmin, avg
     note: str = field(default="", compare=False)
 
     @property
