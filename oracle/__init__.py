@@ -9,4 +9,6 @@ from .vsa_oracle import (  # noqa: F401
     tile_scores, keep_count, select_topk, allowed_tiles, softmax_attention,
     sparse_attention, dense_attention, effective_flops, head_forward,
     segment_tiles, allowed_two_stream, teacher_tile_map, tile_recall,
+    E4M3_MAX, e4m3_round, tile_scale_exponent, quantize_tiles_e4m3, ungather,
+    fp8_attention_inputs,
 )

@@ -18,6 +18,9 @@ order, with the pages' notation where they have one:
   6. mask              prefix keys and prefix query rows always dense
   7. attention         softmax attention over the allowed real keys
 
+and, outside that order: the two-stream budget (8), the teacher tile map
+and tile recall (9), and the fp8 e4m3 attention inputs (10).
+
 Where the pages leave a step open, the reading taken is stated in the
 function's docstring (the full list of readings is in the design notes).
 
@@ -414,6 +417,86 @@ def tile_recall(selection, teacher_rows, k: int) -> float:
     sel = np.asarray(selection)
     hits = [len(set(a[:k].tolist()) & set(b.tolist())) for a, b in zip(sel, top)]
     return float(np.mean(hits)) / k
+
+
+# --------------------------------------------------------------------------
+# 10. Low-precision attention inputs (fp8 e4m3)
+# --------------------------------------------------------------------------
+
+E4M3_MAX = 448.0          # largest finite OCP e4m3 value, 1.75 * 2^8
+
+
+def e4m3_round(x) -> np.ndarray:
+    """Round to the nearest OCP FP8 E4M3 value, ties to even (float64 out).
+
+    E4M3: 1 sign, 4 exponent bits (bias 7), 3 mantissa bits; normals
+    2^-6 .. 448, subnormals in steps of 2^-9. The node runs its attention as
+    a quantized kernel ("Veda Sparse Attention в ComfyUI", section "Узел
+    ComfyUI": a Triton INT8 kernel); the MI355X analogue is the e4m3 matrix
+    core format. Reading: inputs beyond +-448 are an error here (the
+    quantizer scales every tile into range first).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(~np.isfinite(x)) or np.any(np.abs(x) > E4M3_MAX):
+        raise ValueError("e4m3_round: value outside the finite e4m3 range")
+    ax = np.abs(x)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    e = np.maximum(e, -6.0)                      # below 2^-6: the subnormal grid
+    step = np.exp2(e - 3.0)                      # 3 mantissa bits
+    r = np.round(ax / step) * step               # np.round: half to even; exact
+    return np.copysign(r, x)
+
+
+def tile_scale_exponent(amax: float) -> int:
+    """Per-tile power-of-two scale: the least e with amax * 2^-e <= 448.
+
+    Reading: one scale per 64-token tile of a head, a power of two so that
+    scaling is exact (the OCP microscaling formats use power-of-two scales
+    too); e = 0 for an all-zero tile.
+    """
+    amax = float(amax)
+    if amax == 0.0:
+        return 0
+    m, E = math.frexp(amax)                      # amax = m * 2^E, 0.5 <= m < 1
+    return E - 9 if m <= 0.875 else E - 8        # 448 = 0.875 * 2^9
+
+
+def quantize_tiles_e4m3(xt: np.ndarray):
+    """Tiled rows [n_tiles, 64, d] -> (dequantized values, exponents).
+
+    Each tile is scaled by 2^-e (tile_scale_exponent of its largest |x|,
+    pads are zero), rounded to e4m3, and scaled back: the value the fp8
+    path computes with is e4m3_round(x * 2^-e) * 2^e exactly.
+    """
+    xt = np.asarray(xt, dtype=np.float64)
+    exps = np.array([tile_scale_exponent(np.abs(t).max()) for t in xt], dtype=np.int64)
+    sc = np.exp2(exps.astype(np.float64))[:, None, None]
+    return e4m3_round(xt / sc) * sc, exps
+
+
+def ungather(xt: np.ndarray, tmap: TileMap, n_tokens: int) -> np.ndarray:
+    """Inverse of gather: tile rows back to token order (pads dropped)."""
+    s2t = tmap.slot_to_token
+    flat = np.asarray(xt).reshape(-1, np.asarray(xt).shape[-1])
+    out = np.zeros((n_tokens, flat.shape[1]), dtype=flat.dtype)
+    real = s2t >= 0
+    out[s2t[real]] = flat[real]
+    return out
+
+
+def fp8_attention_inputs(q, k, v, tmap: TileMap):
+    """Q, K, V as the fp8 path sees them: per-tile e4m3 values, token order.
+
+    Attention over these with the same mask (sparse_attention) is what the
+    fp8 kernel computes, up to its rounding of the probabilities.
+    """
+    n = np.asarray(q).shape[0]
+    out = []
+    for x in (q, k, v):
+        xq, _ = quantize_tiles_e4m3(gather(np.asarray(x, dtype=np.float64), tmap))
+        out.append(ungather(xq, tmap, n))
+    return tuple(out)
 
 
 # --------------------------------------------------------------------------

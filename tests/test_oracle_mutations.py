@@ -13,6 +13,7 @@ import pytest
 import oracle
 import oracle.vsa_oracle as vo
 from tests import test_oracle_attention as ta
+from tests import test_oracle_fp8 as tf8
 from tests import test_oracle_map as tm_
 from tests import test_oracle_pool_score as tp
 from tests import test_oracle_select as ts
@@ -111,6 +112,25 @@ def _recall_over_n(selection, teacher_rows, k):
     return _orig_recall(selection, teacher_rows, k) * k / np.asarray(teacher_rows).shape[1]
 
 
+def _e4m3_ties_away(x):
+    x = np.asarray(x, dtype=np.float64)
+    ax = np.abs(x)
+    e = np.maximum(np.floor(np.log2(np.where(ax > 0, ax, 1.0))), -6.0)
+    step = np.exp2(e - 3.0)
+    return np.copysign(np.floor(ax / step + 0.5) * step, x)
+
+
+def _scale_exponent_plus_one(amax):
+    return _orig_scale_exp(amax) + (1 if amax else 0)
+
+
+def _quantize_per_tensor(xt):
+    xt = np.asarray(xt, dtype=np.float64)
+    e = _orig_scale_exp(np.abs(xt).max())
+    return vo.e4m3_round(xt * 2.0 ** -e) * 2.0 ** e, np.full(len(xt), e, dtype=np.int64)
+
+
+_orig_scale_exp = vo.tile_scale_exponent
 _orig_recall = vo.tile_recall
 _orig_two_stream = vo.allowed_two_stream
 _orig_segment_tiles = vo.segment_tiles
@@ -148,6 +168,10 @@ CASES = [
     ("segment_tiles", _segment_tiles_shifted, tts.test_segment_tiles_follow_the_tile_map),
     ("teacher_tile_map", _teacher_max_logit, tte.test_teacher_map_by_brute_force),
     ("tile_recall", _recall_over_n, tte.test_tile_recall_hand_cases),
+    ("e4m3_round", _e4m3_ties_away, tf8.test_e4m3_code_table_fixed_points_and_even_ties),
+    ("tile_scale_exponent", _scale_exponent_plus_one, tf8.test_tile_scale_exponent_brute_force),
+    ("quantize_tiles_e4m3", _quantize_per_tensor,
+     tf8.test_quantize_tiles_error_bound_and_per_tile_scale),
 ]
 
 
