@@ -453,13 +453,16 @@ def tile_scale_exponent(amax: float) -> int:
 
     Reading: one scale per 64-token tile of a head, a power of two so that
     scaling is exact (the OCP microscaling formats use power-of-two scales
-    too); e = 0 for an all-zero tile.
+    too); e = 0 for an all-zero tile. The scale is kept as a biased 8-bit
+    exponent (the microscaling E8M0 byte), so e is clamped to >= -127: a
+    tile whose largest |x| is below 448 * 2^-127 keeps e = -127.
     """
     amax = float(amax)
     if amax == 0.0:
         return 0
     m, E = math.frexp(amax)                      # amax = m * 2^E, 0.5 <= m < 1
-    return E - 9 if m <= 0.875 else E - 8        # 448 = 0.875 * 2^9
+    e = E - 9 if m <= 0.875 else E - 8           # 448 = 0.875 * 2^9
+    return max(e, -127)
 
 
 def quantize_tiles_e4m3(xt: np.ndarray):

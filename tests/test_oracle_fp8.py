@@ -63,8 +63,14 @@ def test_tile_scale_exponent_brute_force():
     for a in amaxes:
         e = oracle.tile_scale_exponent(a)
         assert math.ldexp(a, -e) <= 448.0          # in range
-        assert math.ldexp(a, -(e - 1)) > 448.0     # and e is the least such
+        if e > -127:
+            assert math.ldexp(a, -(e - 1)) > 448.0     # and e is the least such
+        else:                                      # clamped: the scale byte's floor
+            assert a <= math.ldexp(448.0, -127)
     assert oracle.tile_scale_exponent(0.0) == 0
+    assert oracle.tile_scale_exponent(2.0 ** -149) == -127
+    assert oracle.tile_scale_exponent(math.ldexp(448.0, -127)) == -127
+    assert oracle.tile_scale_exponent(math.ldexp(449.0, -127)) == -126
 
 
 def test_quantize_tiles_error_bound_and_per_tile_scale():
