@@ -229,4 +229,47 @@ VSA_API int vsa_teacher_map(const vsa_problem *prob, const void *qt, const void 
                                    (hipStream_t)stream));
 }
 
+VSA_API int vsa_quantize_fp8(const vsa_problem *prob, const void *qt, const void *kt,
+                             const void *vt, void *q8, void *k8, void *v8, void *scales,
+                             void *stream) {
+  Plan p;
+  int st = make_plan_geometry(prob, &p);
+  if (st != VSA_OK) return st;
+  if (p.dtype != VSA_BF16) return VSA_ERR_UNSUPPORTED;
+  if (!qt || !kt || !vt || !q8 || !k8 || !v8 || !scales) return VSA_ERR_INVALID_ARG;
+  if (!aligned16(qt) || !aligned16(kt) || !aligned16(vt) || !aligned16(q8) || !aligned16(k8) ||
+      !aligned16(v8) || ((uintptr_t)scales & 3u))
+    return VSA_ERR_INVALID_ARG;
+  return hip_status(launch_quant_fp8(p, qt, kt, vt, (uint8_t *)q8, (uint8_t *)k8,
+                                     (uint8_t *)v8, (uint8_t *)scales, (hipStream_t)stream));
+}
+
+VSA_API int vsa_sparse_attn_fwd_fp8(const vsa_problem *prob, const void *q8, const void *k8,
+                                    const void *v8, const void *scales,
+                                    const int32_t *slot_to_token, const int32_t *kv_idx,
+                                    double sparsity, const vsa_ref_budget *budget,
+                                    const int32_t *ref_idx, float softmax_scale, void *out,
+                                    float *lse, void *stream) {
+  Plan p;
+  int st = make_plan(prob, sparsity, &p);
+  if (st != VSA_OK) return st;
+  if (p.dtype != VSA_BF16) return VSA_ERR_UNSUPPORTED;
+  if (budget) {
+    if (p.dense || !ref_idx) return VSA_ERR_INVALID_ARG;
+    st = apply_ref_budget(budget, &p);
+    if (st != VSA_OK) return st;
+  }
+  if (!q8 || !k8 || !v8 || !scales || !slot_to_token || !out) return VSA_ERR_INVALID_ARG;
+  if (!p.dense && !kv_idx) return VSA_ERR_INVALID_ARG;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(out) ||
+      ((uintptr_t)scales & 3u))
+    return VSA_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale)) return VSA_ERR_INVALID_ARG;
+  float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)p.d);
+  return hip_status(vsa::launch_attn_fp8(p, (const uint8_t *)q8, (const uint8_t *)k8,
+                                         (const uint8_t *)v8, (const uint8_t *)scales,
+                                         slot_to_token, kv_idx, ref_idx, scale, out, lse,
+                                         (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -65,3 +65,14 @@ hipError_t launch_attention(const Plan &p, const void *qt, const void *kt,
 // the largest attention probability per video tile pair into teacher).
 hipError_t launch_teacher(const Plan &p, const void *qt, const void *kt, const int32_t *s2t,
                           float scale, float *lse_ws, float *teacher, hipStream_t stream);
+// fp8 path: per-tile power-of-two scaled E4M3 copies of the bf16 tiles (and
+// their scale bytes, 4 per (batch*head, tile)), then attention over them.
+hipError_t launch_quant_fp8(const Plan &p, const void *qt, const void *kt, const void *vt,
+                            uint8_t *q8, uint8_t *k8, uint8_t *v8, uint8_t *scales,
+                            hipStream_t stream);
+namespace vsa {
+hipError_t launch_attn_fp8(const Plan &p, const uint8_t *q8, const uint8_t *k8,
+                           const uint8_t *v8, const uint8_t *scales, const int32_t *s2t,
+                           const int32_t *kv_idx, const int32_t *ref_idx, float scale,
+                           void *out, float *lse, hipStream_t stream);
+}  // namespace vsa

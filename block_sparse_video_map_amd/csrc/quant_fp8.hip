@@ -1,0 +1,123 @@
+// fp8 inputs of the low-precision attention path: every bf16 Q, K and V tile
+// of a head is scaled by a power of two 2^-e (the least e that brings the
+// tile's largest |x| to at most 448, the largest E4M3 value; e = 0 for an
+// all-zero tile, e >= -127 so that e + 127 fits the scale byte), rounded to
+// OCP E4M3 (nearest, ties to even) and written in the fp8 operand layouts.
+// The node runs its attention as a quantized kernel ("Veda Sparse Attention
+// в ComfyUI", section "Узел ComfyUI"); E4M3 is the MI355X matrix core's
+// 8-bit format.
+//
+// One workgroup per (tile, batch*head, tensor): the tile is unpacked into
+// LDS in plain slot-major order while its largest |x| is reduced, then every
+// thread packs 16-byte chunks of the output layout from LDS.
+#include "device_common.h"
+#include "fp8_layout.h"
+#include "kernels.h"
+
+namespace vsa {
+namespace {
+
+constexpr int kQThreads = 256;
+
+__device__ inline uint32_t pack4_fp8(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);     // bytes 0, 1
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);          // bytes 2, 3
+  return (uint32_t)w;
+}
+
+template <int D>
+__global__ __launch_bounds__(kQThreads) void quant_fp8_kernel(
+    Plan p, const bf16_bits *__restrict__ qt, const bf16_bits *__restrict__ kt,
+    const bf16_bits *__restrict__ vt, uint8_t *__restrict__ q8, uint8_t *__restrict__ k8,
+    uint8_t *__restrict__ v8, uint8_t *__restrict__ exps) {
+  constexpr int LD = D + 8;                    // bf16 row stride in LDS
+  __shared__ bf16_bits xs[kTile * LD];
+  __shared__ float wmax[kQThreads / 64];
+  const int tile = blockIdx.x, bh = blockIdx.y, which = blockIdx.z;
+  const int h = bh % p.H, s = h % p.n_shapes;
+  if (tile >= p.n_tiles[s]) return;
+  const int64_t off = ((int64_t)bh * p.max_tiles + tile) * (kTile * D);
+  const bf16_bits *src = (which == 0 ? qt : which == 1 ? kt : vt) + off;
+  uint8_t *dst = (which == 0 ? q8 : which == 1 ? k8 : v8) + off;
+
+  float amax = 0.f;
+  for (int vec = threadIdx.x; vec < kTile * D / 8; vec += kQThreads) {
+    const uint4 raw = *reinterpret_cast<const uint4 *>(src + vec * 8);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int e8 = 0; e8 < 8; ++e8) {
+      const bf16_bits u = (bf16_bits)(w[e8 / 2] >> (16 * (e8 % 2)));
+      int sl, c;
+      if (which == 2)
+        col_layout_decode(vec, e8, D, sl, c);
+      else
+        row_layout_decode(vec, e8, D, sl, c);
+      xs[sl * LD + c] = u;
+      amax = fmaxf(amax, fabsf(bf16_to_float(u)));
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  if (threadIdx.x % 64 == 0) wmax[threadIdx.x / 64] = amax;
+  __syncthreads();
+  amax = wmax[0];
+#pragma unroll
+  for (int w = 1; w < kQThreads / 64; ++w) amax = fmaxf(amax, wmax[w]);
+
+  // amax = m * 2^E, 0.5 <= m < 1, and 448 = 0.875 * 2^9.
+  int e = 0;
+  if (amax > 0.f) {
+    int E;
+    const float m = frexpf(amax, &E);
+    e = m <= 0.875f ? E - 9 : E - 8;
+    e = e < -kFp8ExpBias ? -kFp8ExpBias : e;
+  }
+
+  // Output chunk ch = bytes 16*ch .. 16*ch+15 = block ch/128, half (ch/64)%2,
+  // lane ch%64 of the fp8 layout.
+  for (int ch = threadIdx.x; ch < kTile * D / 16; ch += kQThreads) {
+    const int blk = ch / 128, half = (ch / 64) % 2, lane = ch % 64, g = lane / 32;
+    float x[16];
+    if (which == 2) {
+      const int c = blk * 32 + lane % 32;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = half * 32 + 8 * (j / 4) + 4 * g + j % 4;
+        x[j] = bf16_to_float(xs[key * LD + c]);
+      }
+    } else {
+      const int slot = (blk / (D / 64)) * 32 + lane % 32;
+      const int c0 = (blk % (D / 64)) * 64 + 32 * g + 16 * half;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) x[j] = bf16_to_float(xs[slot * LD + c0 + j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = ldexpf(x[j], -e);    // exact: a power of two
+    uint4 o;
+    o.x = pack4_fp8(x[0], x[1], x[2], x[3]);
+    o.y = pack4_fp8(x[4], x[5], x[6], x[7]);
+    o.z = pack4_fp8(x[8], x[9], x[10], x[11]);
+    o.w = pack4_fp8(x[12], x[13], x[14], x[15]);
+    *reinterpret_cast<uint4 *>(dst + ch * 16) = o;
+  }
+  if (threadIdx.x == 0)
+    exps[((int64_t)bh * p.max_tiles + tile) * 4 + which] = (uint8_t)(e + kFp8ExpBias);
+}
+
+}  // namespace
+}  // namespace vsa
+
+hipError_t launch_quant_fp8(const Plan &p, const void *qt, const void *kt, const void *vt,
+                            uint8_t *q8, uint8_t *k8, uint8_t *v8, uint8_t *exps,
+                            hipStream_t stream) {
+  dim3 grid(p.max_tiles, p.B * p.H, 3);
+  const bf16_bits *q = (const bf16_bits *)qt, *k = (const bf16_bits *)kt,
+                  *v = (const bf16_bits *)vt;
+  if (p.d == 128)
+    hipLaunchKernelGGL(vsa::quant_fp8_kernel<128>, grid, dim3(vsa::kQThreads), 0, stream, p, q,
+                       k, v, q8, k8, v8, exps);
+  else
+    hipLaunchKernelGGL(vsa::quant_fp8_kernel<64>, grid, dim3(vsa::kQThreads), 0, stream, p, q,
+                       k, v, q8, k8, v8, exps);
+  return hipGetLastError();
+}

@@ -26,7 +26,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 # Sources whose text decides the attention kernel's memory traffic.
-ATTN_SOURCES = ("csrc/attn_bf16.hip", "csrc/device_common.h")
+ATTN_SOURCES = ("csrc/attn_bf16.hip", "csrc/attn_common.h", "csrc/device_common.h")
 
 
 def source_hash(files=ATTN_SOURCES) -> str:

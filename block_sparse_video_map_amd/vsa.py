@@ -31,7 +31,8 @@ EXPORTS = ("vsa_query_sizes", "vsa_pooled_bytes", "vsa_map_tiles", "vsa_tile_sco
            "vsa_select_topk", "vsa_sparse_attn_fwd", "vsa_kept_stats",
            "vsa_count_flops", "vsa_ref_sizes", "vsa_ref_pooled_bytes", "vsa_ref_scores",
            "vsa_ref_select", "vsa_sparse_attn_fwd_ref", "vsa_kept_stats_ref",
-           "vsa_count_flops_ref", "vsa_teacher_map", "vsa_status_string", "vsa_version")
+           "vsa_count_flops_ref", "vsa_teacher_map", "vsa_quantize_fp8",
+           "vsa_sparse_attn_fwd_fp8", "vsa_status_string", "vsa_version")
 
 
 class vsa_problem(ctypes.Structure):
@@ -100,6 +101,8 @@ def lib() -> ctypes.CDLL:
             "vsa_kept_stats_ref": [P, f64, R, ctypes.POINTER(i64), ctypes.POINTER(f64)],
             "vsa_count_flops_ref": [P, f64, R, vp, vp, vp, ctypes.POINTER(f64)],
             "vsa_teacher_map": [P, vp, vp, vp, f32, vp, vp, vp],
+            "vsa_quantize_fp8": [P, vp, vp, vp, vp, vp, vp, vp, vp],
+            "vsa_sparse_attn_fwd_fp8": [P, vp, vp, vp, vp, vp, vp, f64, R, vp, f32, vp, vp, vp],
             "vsa_status_string": [ctypes.c_int],
             "vsa_version": [],
         }
@@ -392,17 +395,65 @@ def vsa_teacher_map(prob: Problem, qt, kt, slot_to_token, softmax_scale: float, 
         _ptr(teacher), _stream(stream)))
 
 
+# ------------------------------------------------------------- fp8 variant
+
+def fp8_scale_bytes(prob: Problem) -> int:
+    """Bytes of the per-tile scale array: 4 per (batch, head, tile)."""
+    sz = vsa_query_sizes(prob, 0.0)
+    return prob.B * prob.H * sz.max_tiles * 4
+
+
+def vsa_quantize_fp8(prob: Problem, qt, kt, vt, q8, k8, v8, scales, stream=None):
+    """E4M3 copies of the bf16 tiles (uint8 tensors of tiled_elems) and their
+    per-tile scale bytes (uint8, fp8_scale_bytes)."""
+    import torch
+    sz = vsa_query_sizes(prob, 0.0)
+    et = _elem_dtype(prob)
+    for name, x in (("qt", qt), ("kt", kt), ("vt", vt)):
+        _need(x, sz.tiled_elems, et, name)
+    for name, x in (("q8", q8), ("k8", k8), ("v8", v8)):
+        _need(x, sz.tiled_elems, torch.uint8, name)
+    _need(scales, fp8_scale_bytes(prob), torch.uint8, "scales")
+    _check("vsa_quantize_fp8", lib().vsa_quantize_fp8(
+        prob.ref, _ptr(qt), _ptr(kt), _ptr(vt), _ptr(q8), _ptr(k8), _ptr(v8), _ptr(scales),
+        _stream(stream)))
+
+
+def vsa_sparse_attn_fwd_fp8(prob: Problem, q8, k8, v8, scales, slot_to_token, kv_idx,
+                            sparsity: float, softmax_scale: float, out, lse=None,
+                            budget: Optional[vsa_ref_budget] = None, ref_idx=None,
+                            stream=None):
+    import torch
+    sz = vsa_query_sizes(prob, sparsity)
+    for name, x in (("q8", q8), ("k8", k8), ("v8", v8)):
+        _need(x, sz.tiled_elems, torch.uint8, name)
+    _need(scales, fp8_scale_bytes(prob), torch.uint8, "scales")
+    _need(out, sz.out_elems, torch.bfloat16, "out")
+    _need(lse, prob.B * prob.H * prob.N, torch.float32, "lse")
+    if kv_idx is not None:
+        _need(kv_idx, sz.idx_elems, torch.int32, "kv_idx")
+    if budget is not None:
+        _, _, ie = vsa_ref_sizes(prob, budget)
+        _need(ref_idx, ie, torch.int32, "ref_idx")
+    _check("vsa_sparse_attn_fwd_fp8", lib().vsa_sparse_attn_fwd_fp8(
+        prob.ref, _ptr(q8), _ptr(k8), _ptr(v8), _ptr(scales), _ptr(slot_to_token), _ptr(kv_idx),
+        float(sparsity), None if budget is None else ctypes.byref(budget), _ptr(ref_idx),
+        float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream)))
+
+
 # ---------------------------------------------------------- whole-layer helper
 
 class Layer:
     """Device buffers for one layer and the four calls in order.
 
     Allocates with torch on the current device: slot_to_token, tiled Q/K/V,
-    the pooling workspace, scores, kv_idx, out and lse.
+    the pooling workspace, scores, kv_idx, out and lse. ``fp8=True`` adds the
+    E4M3 tile copies and runs attention on them (bf16 problems only).
     """
 
     def __init__(self, prob: Problem, sparsity: float, mode: int, proj_dim: int,
-                 device="cuda", with_lse: bool = True, ref: Optional[Tuple[int, int]] = None):
+                 device="cuda", with_lse: bool = True, ref: Optional[Tuple[int, int]] = None,
+                 fp8: bool = False):
         import torch
         self.prob, self.sparsity, self.mode, self.proj_dim = prob, sparsity, mode, proj_dim
         self.sizes = sz = vsa_query_sizes(prob, sparsity)
@@ -428,9 +479,20 @@ class Layer:
             self.ref_pooled = torch.empty((rb + 7) // 8, dtype=torch.float64, device=dev)
             self.ref_scores = torch.empty(se, dtype=torch.float32, device=dev)
             self.ref_idx = torch.empty(ie, dtype=torch.int32, device=dev)
+        self.fp8 = fp8
+        if fp8:
+            if prob.dtype != "bf16":
+                raise ValueError("the fp8 variant takes bf16 problems")
+            self.q8, self.k8, self.v8 = (torch.empty(sz.tiled_elems, dtype=torch.uint8,
+                                                     device=dev) for _ in range(3))
+            self.fp8_scales = torch.empty(fp8_scale_bytes(prob), dtype=torch.uint8, device=dev)
 
     def map_tiles(self, q, k, v, stream=None):
         vsa_map_tiles(self.prob, q, k, v, self.slot_to_token, self.qt, self.kt, self.vt, stream)
+
+    def quantize(self, stream=None):
+        vsa_quantize_fp8(self.prob, self.qt, self.kt, self.vt, self.q8, self.k8, self.v8,
+                         self.fp8_scales, stream)
 
     def tile_scores(self, wq, wk, stream=None):
         vsa_tile_scores(self.prob, self.mode, self.proj_dim, self.qt, self.kt,
@@ -447,6 +509,15 @@ class Layer:
 
     def attend(self, softmax_scale: float = 0.0, stream=None, kv_idx=None, ref_idx=None):
         kv = self.kv_idx if kv_idx is None else kv_idx
+        if self.fp8:
+            rf = None
+            if self.budget is not None:
+                rf = self.ref_idx if ref_idx is None else ref_idx
+            vsa_sparse_attn_fwd_fp8(self.prob, self.q8, self.k8, self.v8, self.fp8_scales,
+                                    self.slot_to_token, None if self.sparsity == 0.0 else kv,
+                                    self.sparsity, softmax_scale, self.out, self.lse,
+                                    self.budget, rf, stream)
+            return
         if self.budget is not None:
             rf = self.ref_idx if ref_idx is None else ref_idx
             vsa_sparse_attn_fwd_ref(self.prob, self.qt, self.kt, self.vt, self.slot_to_token, kv,
@@ -460,6 +531,8 @@ class Layer:
     def forward(self, q, k, v, wq, wk, softmax_scale: float = 0.0, stream=None):
         """One whole layer: map+gather, scores, top-k, attention."""
         self.map_tiles(q, k, v, stream)
+        if self.fp8:
+            self.quantize(stream)
         if self.sparsity != 0.0:
             self.tile_scores(wq, wk, stream)
             self.select(stream)

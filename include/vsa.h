@@ -342,6 +342,50 @@ VSA_API int vsa_teacher_map(const vsa_problem *prob, const void *qt, const void 
                             const int32_t *slot_to_token, float softmax_scale, float *lse_ws,
                             float *teacher, void *stream);
 
+/*
+ * vsa_quantize_fp8 - inputs of the low-precision (fp8) attention variant.
+ * The node runs its attention as a quantized kernel ("Veda Sparse Attention
+ * в ComfyUI", section "Узел ComfyUI"); here the format is OCP FP8 E4M3,
+ * the MI355X matrix core's 8-bit type.
+ *
+ * Every tile of every head of qt, kt, vt (bf16, as written by vsa_map_tiles)
+ * gets one power-of-two scale 2^e: e is the least integer with
+ * max|x| * 2^-e <= 448 (e = 0 for an all-zero tile; e >= -127). The tile's
+ * values x * 2^-e are rounded to E4M3 (nearest, ties to even).
+ *
+ * q8, k8, v8: device, tiled_elems BYTES each (same tile order as qt), in the
+ *   fp8 operand layouts: Q and K tiles are 2 KB blocks of 32 slots x 64
+ *   channels, block (s/32)*(d/64) + c/64; V tiles are 2 KB blocks of
+ *   64 keys x 32 channels, block c/32. Inside a block, lane L (0..63) holds
+ *   32 bytes as two 16-byte halves at half*1024 + L*16:
+ *     Q/K: L = s%32 + 32*g, byte e (half e/16, e%16 within it) is channel
+ *          64*(c/64) + 32*g + e;
+ *     V:   L = c%32 + 32*g, byte e is key (e/16)*32 + 8*((e%16)/4) + 4*g + e%4.
+ * scales: device uint8 [B][H][max_tiles][4], byte 0/1/2 = e + 127 of the Q/K/V
+ *   tile, byte 3 unused; 4-byte aligned.
+ * Only tiles that exist for the head's shape are written. dtype must be
+ * VSA_BF16 (VSA_ERR_UNSUPPORTED otherwise).
+ */
+VSA_API int vsa_quantize_fp8(const vsa_problem *prob, const void *qt, const void *kt,
+                             const void *vt, void *q8, void *k8, void *v8, void *scales,
+                             void *stream);
+
+/*
+ * vsa_sparse_attn_fwd_fp8 - step 4 on the fp8 copies: the same key-tile
+ * lists, mask and outputs as vsa_sparse_attn_fwd (budget == NULL) or
+ * vsa_sparse_attn_fwd_ref (budget and ref_idx given), computed from the E4M3
+ * values times their tile scales. Probabilities are rounded to E4M3 before
+ * the PV product (the row max is kept 8 below the true max, so they lie in
+ * (0, 256]); row sums use the same rounded values. out: bf16 [B][H][N][d];
+ * lse: float [B][H][N] or NULL. dtype must be VSA_BF16.
+ */
+VSA_API int vsa_sparse_attn_fwd_fp8(const vsa_problem *prob, const void *q8, const void *k8,
+                                    const void *v8, const void *scales,
+                                    const int32_t *slot_to_token, const int32_t *kv_idx,
+                                    double sparsity, const vsa_ref_budget *budget,
+                                    const int32_t *ref_idx, float softmax_scale, void *out,
+                                    float *lse, void *stream);
+
 /* Static text for a vsa_status value. */
 VSA_API const char *vsa_status_string(int status);
 

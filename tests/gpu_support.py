@@ -43,6 +43,37 @@ def col_layout_index(d: int) -> np.ndarray:
     return off.reshape(-1)
 
 
+def fp8_row_layout_index(d: int) -> np.ndarray:
+    """perm[s*d + c] = byte offset of (slot s, channel c) in an fp8 Q/K tile."""
+    s = np.arange(64)[:, None]
+    c = np.arange(d)[None, :]
+    w = c % 64
+    off = ((s // 32) * (d // 64) + c // 64) * 2048 + ((w % 32) // 16) * 1024 \
+        + (s % 32 + 32 * (w // 32)) * 16 + w % 16
+    return off.reshape(-1)
+
+
+def fp8_col_layout_index(d: int) -> np.ndarray:
+    """perm[s*d + c] = byte offset of (key s, channel c) in an fp8 V tile."""
+    s = np.arange(64)[:, None]
+    c = np.arange(d)[None, :]
+    w = s % 32
+    g, r = (w // 4) % 2, (w // 8) * 4 + w % 4
+    off = (c // 32) * 2048 + (s // 32) * 1024 + (c % 32 + 32 * g) * 16 + r
+    return off.reshape(-1)
+
+
+def unpack_fp8_tiles(codes: np.ndarray, exps: np.ndarray, n_tiles: int, d: int,
+                     col: bool) -> np.ndarray:
+    """uint8 E4M3 codes in the fp8 layout -> [n_tiles, 64, d] float64 values
+    times 2^exps[tile]."""
+    import torch
+    perm = fp8_col_layout_index(d) if col else fp8_row_layout_index(d)
+    t = np.ascontiguousarray(codes[: n_tiles * 64 * d].reshape(n_tiles, 64 * d)[:, perm])
+    vals = torch.from_numpy(t).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return vals.reshape(n_tiles, 64, d) * np.exp2(exps[:n_tiles].astype(np.float64))[:, None, None]
+
+
 def unpack_tiles(flat: np.ndarray, n_tiles: int, d: int, col: bool) -> np.ndarray:
     """[n_tiles*64*d] tiled layout -> [n_tiles, 64, d] plain rows."""
     perm = col_layout_index(d) if col else row_layout_index(d)
@@ -201,6 +232,13 @@ F32_MAX_ABS = 1e-5
 # the log of the sum is within 2^-9 of the exact LSE, plus fp32 rounding of the
 # logits and the sum.
 BF16_LSE_ABS = 2.0 ** -9 + 1e-4
+# fp8 path, against exact attention over the same E4M3 inputs: the kernel
+# rounds every probability to E4M3 (relative error <= 2^-4) and sums the
+# rounded values; the f8 MFMA sums its 64 products at about 2^-13 relative.
+# A CPU model of the probability rounding (tests/test_fp8_tolerance_model.py)
+# stays within 0.6 of these on the small fp8 test workloads, whose rows see
+# the fewest keys (700 to 2,000; errors shrink as rows see more keys).
+FP8_MAX_ABS, FP8_MEAN_ABS, FP8_LSE_ABS = 5e-2, 4e-3, 2e-2
 
 
 def default_scale(d):

@@ -289,3 +289,50 @@ def test_ref_kept_stats_and_flops_match_oracle():
     kept, frac = vsa.vsa_kept_stats_ref(p, 0.5, budget)
     assert kept == sum(int(a.sum()) for a in allows)
     assert math.isclose(frac, kept / (w.H * tm.n_tiles ** 2), rel_tol=1e-12)
+
+
+# ------------------------------------------------------------ fp8 variant
+
+def test_fp8_entry_points_reject_before_any_launch():
+    """Argument errors come back from the host checks (no device pointer is
+    dereferenced: the pointers below are never valid device memory)."""
+    L = vsa.lib()
+    fake = ctypes.c_void_p(1 << 20)                     # 16-byte aligned, never read
+    w = WORKLOADS["1"]                                  # f32 problem
+    p32 = _problem(w)
+    assert L.vsa_quantize_fp8(p32.ref, fake, fake, fake, fake, fake, fake, fake,
+                              None) == vsa.VSA_ERR_UNSUPPORTED
+    assert L.vsa_sparse_attn_fwd_fp8(p32.ref, fake, fake, fake, fake, fake, fake,
+                                     ctypes.c_double(0.5), None, None, ctypes.c_float(0.0),
+                                     fake, None, None) == vsa.VSA_ERR_UNSUPPORTED
+    pb = _problem(w, dtype="bf16")
+    # missing buffers
+    assert L.vsa_quantize_fp8(pb.ref, fake, fake, None, fake, fake, fake, fake,
+                              None) == vsa.VSA_ERR_INVALID_ARG
+    # scales not 4-byte aligned
+    assert L.vsa_quantize_fp8(pb.ref, fake, fake, fake, fake, fake, fake,
+                              ctypes.c_void_p((1 << 20) + 2), None) == vsa.VSA_ERR_INVALID_ARG
+    # sparse path without kv_idx; budget without ref_idx; budget on the dense path
+    assert L.vsa_sparse_attn_fwd_fp8(pb.ref, fake, fake, fake, fake, fake, None,
+                                     ctypes.c_double(0.5), None, None, ctypes.c_float(0.0),
+                                     fake, None, None) == vsa.VSA_ERR_INVALID_ARG
+    rb = vsa.ref_budget(1, 1)
+    assert L.vsa_sparse_attn_fwd_fp8(pb.ref, fake, fake, fake, fake, fake, fake,
+                                     ctypes.c_double(0.5), ctypes.byref(rb), None,
+                                     ctypes.c_float(0.0), fake, None,
+                                     None) == vsa.VSA_ERR_INVALID_ARG
+    assert L.vsa_sparse_attn_fwd_fp8(pb.ref, fake, fake, fake, fake, fake, fake,
+                                     ctypes.c_double(0.0), ctypes.byref(rb), fake,
+                                     ctypes.c_float(0.0), fake, None,
+                                     None) == vsa.VSA_ERR_INVALID_ARG
+    assert L.vsa_sparse_attn_fwd_fp8(pb.ref, fake, fake, fake, fake, fake, fake,
+                                     ctypes.c_double(0.5), None, None,
+                                     ctypes.c_float(float("nan")), fake, None,
+                                     None) == vsa.VSA_ERR_INVALID_ARG
+
+
+def test_fp8_scale_bytes():
+    w = WORKLOADS["3a"]
+    p = _problem(w)
+    sz = vsa.vsa_query_sizes(p, w.sparsity)
+    assert vsa.fp8_scale_bytes(p) == w.B * w.H * sz.max_tiles * 4

@@ -1,0 +1,165 @@
+"""GPU parity of the fp8 (E4M3) attention variant against the oracle.
+
+The quantizer must be bit-exact: every tile's scale exponent and every E4M3
+value equal to oracle.quantize_tiles_e4m3 on the same bf16 tiles. Attention
+outputs are compared, on the GPU's own selections, with exact attention over
+the oracle's E4M3 inputs, within the fp8 tolerances (the kernel rounds the
+probabilities to E4M3; see tests/gpu_support.py). Ragged grids, prefix
+segments, head-aware shapes, d = 64 and 128, the two-stream budget, the dense
+path and sampled query tiles at the full-clip shape.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from tests import gpu_support as gs
+from workloads import WORKLOADS
+from workloads.configs import HEAD_AWARE_CYCLE, Workload
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "mg-d128": Workload("f8-mg", "bf16", 2, 2, 128, (5, 16, 20), (40, 300, 24),
+                        ((4, 4, 4),), "mean_gate", 0.75, 4201),
+    "tp-d128": Workload("f8-tp", "bf16", 1, 3, 128, (5, 16, 20), (100, 700, 30),
+                        HEAD_AWARE_CYCLE, "trippool", 0.8, 4202),
+    "mg-d64": Workload("f8-d64", "bf16", 1, 2, 64, (3, 9, 14), (40, 150, 24),
+                       ((4, 4, 4),), "mean_gate", 0.5, 4203),
+}
+
+
+def _run(w, sparsity=None, ref=None):
+    import torch
+    from block_sparse_video_map_amd import vsa
+    sp = w.sparsity if sparsity is None else sparsity
+    prob = gs.problem_of(w)
+    layer = vsa.Layer(prob, sp, vsa.score_mode(w.scorer, w.tripool_mode),
+                      w.d if w.scorer == "mean_gate" else w.proj_dim, ref=ref, fp8=True)
+    q, k, v = gs.to_device(w)
+    from workloads.inputs import make_weights
+    W = make_weights(w)
+    if w.scorer == "mean_gate":
+        wq, wk = torch.from_numpy(W["gate"]).cuda(), None
+    else:
+        wq, wk = torch.from_numpy(W["proj_q"]).cuda(), torch.from_numpy(W["proj_k"]).cuda()
+    layer.forward(q, k, v, wq, wk)
+    torch.cuda.synchronize()
+    return layer
+
+
+def _selection(w, layer, b, h, nv):
+    sz = layer.sizes
+    kv = layer.kv_idx[: sz.idx_elems].view(w.B * w.H, sz.max_video_tiles, sz.k_max)
+    return kv[b * w.H + h, :nv].cpu().numpy()
+
+
+def _compare(w, layer, b, h, allow, tm, query_tiles=None, label=""):
+    q, k, v = gs.head_inputs(w, h, b)
+    qq, kq, vq = oracle.fp8_attention_inputs(q, k, v, tm)
+    want, lse_want = oracle.sparse_attention(qq, kq, vq, tm, allow, 1.0 / np.sqrt(w.d),
+                                             query_tiles)
+    rows = np.nonzero(~np.isnan(want[:, 0]))[0]
+    got = gs.tensor_f32(layer.out[b, h])[rows]
+    mx, mean = gs.bf16_stats(got, want[rows])
+    lse_err = float(np.abs(layer.lse[b, h].cpu().numpy()[rows] - lse_want[rows]).max())
+    gs.log(f"[fp8] {w.name}{label} b{b} h{h}: rows {rows.size} max-abs {mx:.2e} "
+           f"mean-abs {mean:.2e} lse {lse_err:.2e}")
+    assert mx <= gs.FP8_MAX_ABS and mean <= gs.FP8_MEAN_ABS and lse_err <= gs.FP8_LSE_ABS
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_quantize_fp8_bit_exact(name):
+    w = SMALL[name]
+    gs.log(f"[fp8] quantize {name}")
+    layer = _run(w)
+    sz = layer.sizes
+    per_head = sz.max_tiles * 64 * w.d
+    exps = layer.fp8_scales.cpu().numpy().reshape(w.B * w.H, sz.max_tiles, 4).astype(np.int64)
+    exps -= 127
+    for b in range(w.B):
+        for h in range(w.H):
+            bh = b * w.H + h
+            tm = oracle.tile_map(*w.grid, w.prefix, w.tile_shapes[h % len(w.tile_shapes)])
+            for which, (x, t) in enumerate(zip(gs.head_inputs(w, h, b),
+                                               (layer.q8, layer.k8, layer.v8))):
+                want, we = oracle.quantize_tiles_e4m3(oracle.gather(x, tm))
+                np.testing.assert_array_equal(exps[bh, :tm.n_tiles, which], we)
+                codes = t[bh * per_head:(bh + 1) * per_head].cpu().numpy()
+                got = gs.unpack_fp8_tiles(codes, exps[bh, :, which], tm.n_tiles, w.d,
+                                          col=(which == 2))
+                np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_fp8_attention_parity(name):
+    w = SMALL[name]
+    gs.log(f"[fp8] attention {name}")
+    layer = _run(w)
+    for b in range(w.B):
+        for h in range(w.H):
+            orc, _ = gs.oracle_head(w, h, b=b, query_tiles=[])
+            tm = orc["tmap"]
+            sel = _selection(w, layer, b, h, tm.n_video_tiles)
+            differ, wide, fails = gs.band_rule_check(orc["scores"], sel, orc["k"])
+            assert not fails and differ <= wide
+            allow = oracle.allowed_tiles(tm, sel[:, :orc["k"]])
+            _compare(w, layer, b, h, allow, tm)
+
+
+def test_fp8_dense_path():
+    """sparsity 0: every tile kept, dense attention over the E4M3 inputs."""
+    w = SMALL["mg-d64"]
+    layer = _run(w, sparsity=0.0)
+    for h in range(w.H):
+        tm = oracle.tile_map(*w.grid, w.prefix, w.tile_shapes[h % len(w.tile_shapes)])
+        allow = np.ones((tm.n_tiles, tm.n_tiles), dtype=bool)
+        _compare(w, layer, 0, h, allow, tm, label=" dense")
+
+
+def test_fp8_two_stream():
+    w = SMALL["tp-d128"]
+    ref = (1, 4)
+    layer = _run(w, ref=ref)
+    sz = layer.sizes
+    n_ref = layer.ref_scores.numel() // (w.B * w.H * sz.max_video_tiles)
+    for h in range(w.H):
+        orc, _ = gs.oracle_head(w, h, query_tiles=[], ref=ref)
+        tm = orc["tmap"]
+        nv = tm.n_video_tiles
+        sel = _selection(w, layer, 0, h, nv)[:, :orc["k"]]
+        rsel = layer.ref_idx.view(w.B * w.H, sz.max_video_tiles, ref[1])[h, :nv].cpu().numpy()
+        assert n_ref == orc["ref_tiles"].size
+        allow = oracle.allowed_two_stream(tm, sel, orc["ref_tiles"], rsel)
+        _compare(w, layer, 0, h, allow, tm, label=" two-stream")
+
+
+def test_fp8_full_clip_sampled():
+    """The full-clip shape (24 heads, 1,767 tiles, 25% kept): quantizer on
+    two heads' sampled tiles, attention on sampled query tiles."""
+    import torch
+    w = WORKLOADS["3a"]
+    gs.log("[fp8] full clip")
+    layer = _run(w)
+    sz = layer.sizes
+    per_head = sz.max_tiles * 64 * w.d
+    exps = layer.fp8_scales.cpu().numpy().reshape(w.B * w.H, sz.max_tiles, 4).astype(np.int64)
+    exps -= 127
+    rng = np.random.default_rng(7)
+    for h in (0, 23):
+        tm = oracle.tile_map(*w.grid, w.prefix, w.tile_shapes[h % len(w.tile_shapes)])
+        q, k, v = gs.head_inputs(w, h)
+        tiles = np.sort(rng.choice(tm.n_tiles, 48, replace=False))
+        for which, (x, t) in enumerate(zip((q, k, v), (layer.q8, layer.k8, layer.v8))):
+            want, we = oracle.quantize_tiles_e4m3(oracle.gather(x, tm)[tiles])
+            np.testing.assert_array_equal(exps[h, tiles, which], we)
+            codes = t[h * per_head:(h + 1) * per_head].cpu().numpy()
+            got = gs.unpack_fp8_tiles(codes, exps[h, :, which], tm.n_tiles, w.d, col=(which == 2))
+            np.testing.assert_array_equal(got[tiles], want)
+        sel = _selection(w, layer, 0, h, tm.n_video_tiles)
+        k_h = oracle.keep_count(w.sparsity, tm.n_video_tiles)
+        allow = oracle.allowed_tiles(tm, sel[:, :k_h])
+        qt = list(range(tm.n_prefix_tiles)) + sorted(
+            int(tm.n_prefix_tiles + i) for i in rng.choice(tm.n_video_tiles, 12, replace=False))
+        _compare(w, layer, 0, h, allow, tm, query_tiles=qt, label=" sampled")
+    del layer
+    torch.cuda.empty_cache()
