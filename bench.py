@@ -38,11 +38,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="3a")
-    ap.add_argument("--also", default="3b,3a-h3,3b-r2va",
+    ap.add_argument("--also", default="3b,3a-h3,3b-r2va,3a-fp8",
                     help="extra workloads reported beside, ',' list; a '-h3' suffix keeps "
                          "only heads 0-2 (one GPU's share of 24 heads over 8 GPUs); "
                          "'-r2va' runs the two-stream budget (32 reference tiles of the "
-                         "reference-image segment and 32 video tiles per query tile)")
+                         "reference-image segment and 32 video tiles per query tile); "
+                         "'-fp8' runs the E4M3 attention variant (quantizer included)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="with --profile-attn-only: run the E4M3 variant of the layer")
     ap.add_argument("--dense-steps", type=int, default=2)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -60,7 +63,7 @@ class Case:
     """Library buffers and inputs for one workload, resident on the GPU."""
 
     def __init__(self, wname: str, sparsity=None, heads=None, ref=None, workload=None,
-                 inputs=None):
+                 inputs=None, fp8=False):
         import dataclasses
 
         import numpy as np
@@ -77,7 +80,9 @@ class Case:
         mode = vsa.score_mode(w.scorer, w.tripool_mode)
         proj = w.d if w.scorer == "mean_gate" else w.proj_dim
         self.ref = ref
-        self.layer = vsa.Layer(self.prob, self.sparsity, mode, proj, with_lse=False, ref=ref)
+        self.fp8 = fp8
+        self.layer = vsa.Layer(self.prob, self.sparsity, mode, proj, with_lse=False, ref=ref,
+                               fp8=fp8)
         t0 = time.time()
         bits = w.dtype == "bf16"
         if inputs is not None:                     # device tensors of another case
@@ -136,6 +141,9 @@ class Case:
                L.select, L.attend]
         if self.sparsity == 0.0:
             names, fns = [names[0], names[3]], [fns[0], fns[3]]
+        if self.fp8:
+            names.insert(1, "quantize_fp8")
+            fns.insert(1, L.quantize)
         samples = {n: [] for n in names}
         for _ in range(reps):
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
@@ -285,7 +293,11 @@ def main():
     from workloads import WORKLOADS
 
     w = WORKLOADS[a.workload]
-    case = Case(a.workload)
+    if a.fp8 and not a.profile_attn_only:
+        print("--fp8 only applies to --profile-attn-only (the headline is the bf16 path)",
+              file=sys.stderr)
+        sys.exit(2)
+    case = Case(a.workload, fp8=a.fp8)
     flops = case.flops()
     if a.profile_attn_only:
         case.time_steps(a.steps, a.warmup)
@@ -319,12 +331,14 @@ def main():
 
     extra = {}
     for name in [x for x in a.also.split(",") if x]:
-        heads, ref, sp, label = None, None, None, name
+        heads, ref, sp, label, fp8 = None, None, None, name, False
+        if name.endswith("-fp8"):         # E4M3 attention variant (reduced precision)
+            name, fp8 = name[:-4], True
         if name.endswith("-h3"):          # one GPU's share when 8 GPUs split the heads
             name, heads = name[:-3], 3
         if name.endswith("-r2va"):        # two-stream budget: 32 + 32 tiles per query tile
             name, ref, sp = name[:-5], (1, 32), 0.9819
-        c = Case(name, heads=heads, ref=ref, sparsity=sp)
+        c = Case(name, heads=heads, ref=ref, sparsity=sp, fp8=fp8)
         name = label
         f = c.flops()
         ms = c.time_steps(max(3, a.steps // 2), 2) * 1e3
@@ -333,6 +347,11 @@ def main():
                        "attention_ms": round(mn2["attention"], 4),
                        "effective_tflops_attention": f / mn2["attention"] / 1e9,
                        "effective_tflop": f / 1e12, "stage_ms_median": m2}
+        if fp8:
+            extra[name]["precision"] = ("E4M3 Q/K/V and probabilities, fp32 accumulation, "
+                                        "bf16 output: a reduced-precision variant, not the "
+                                        "headline")
+            extra[name]["frac_of_fp8_peak"] = round(f / mn2["attention"] / 1e9 / 5000.0, 4)
         c.release()
         log(f"[bench] {name}: {ms:.3f} ms/step")
 
