@@ -43,7 +43,8 @@ def parse():
                          "only heads 0-2 (one GPU's share of 24 heads over 8 GPUs); "
                          "'-r2va' runs the two-stream budget (32 reference tiles of the "
                          "reference-image segment and 32 video tiles per query tile); "
-                         "'-fp8' runs the E4M3 attention variant (quantizer included)")
+                         "'-fp8' runs the E4M3 attention variant (its gather also writes the "
+                         "E4M3 tiles)")
     ap.add_argument("--fp8", action="store_true",
                     help="with --profile-attn-only: run the E4M3 variant of the layer")
     ap.add_argument("--dense-steps", type=int, default=2)
@@ -141,9 +142,9 @@ class Case:
                L.select, L.attend]
         if self.sparsity == 0.0:
             names, fns = [names[0], names[3]], [fns[0], fns[3]]
-        if self.fp8:
-            names.insert(1, "quantize_fp8")
-            fns.insert(1, L.quantize)
+        if self.fp8:                       # the gather writes the E4M3 tiles too
+            names[0] = "map_gather_fp8"
+            fns[0] = lambda: L.map_tiles_fp8(self.q, self.k, self.v)
         samples = {n: [] for n in names}
         for _ in range(reps):
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]

@@ -49,7 +49,29 @@ VSA_API int vsa_map_tiles(const vsa_problem *prob, const void *q, const void *k,
   hipError_t e = launch_build_map(p, slot_to_token, s);
   if (e != hipSuccess) return VSA_ERR_HIP;
   if (!q && !k && !v) return VSA_OK;
-  return hip_status(launch_gather(p, q, k, v, slot_to_token, qt, kt, vt, s));
+  return hip_status(launch_gather(p, q, k, v, slot_to_token, qt, kt, vt, nullptr, nullptr,
+                                  nullptr, nullptr, s));
+}
+
+VSA_API int vsa_map_tiles_fp8(const vsa_problem *prob, const void *q, const void *k,
+                              const void *v, int32_t *slot_to_token, void *qt, void *kt,
+                              void *vt, void *q8, void *k8, void *v8, void *scales,
+                              void *stream) {
+  Plan p;
+  int st = make_plan_geometry(prob, &p);
+  if (st != VSA_OK) return st;
+  if (p.dtype != VSA_BF16) return VSA_ERR_UNSUPPORTED;
+  if (!slot_to_token || !q || !k || !v || !qt || !kt || !vt || !q8 || !k8 || !v8 || !scales)
+    return VSA_ERR_INVALID_ARG;
+  const void *al[10] = {q, k, v, qt, kt, vt, q8, k8, v8, nullptr};
+  for (int i = 0; i < 9; ++i)
+    if (!aligned16(al[i])) return VSA_ERR_INVALID_ARG;
+  if ((uintptr_t)scales & 3u) return VSA_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_build_map(p, slot_to_token, s);
+  if (e != hipSuccess) return VSA_ERR_HIP;
+  return hip_status(launch_gather(p, q, k, v, slot_to_token, qt, kt, vt, (uint8_t *)q8,
+                                  (uint8_t *)k8, (uint8_t *)v8, (uint8_t *)scales, s));
 }
 
 VSA_API int vsa_tile_scores(const vsa_problem *prob, int32_t mode, int32_t proj_dim,

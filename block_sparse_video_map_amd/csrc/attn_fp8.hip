@@ -67,11 +67,6 @@ __device__ inline i32x8 lds_operand(const uint8_t *blk, int lane) {
               *reinterpret_cast<const i32x4 *>(blk + 1024 + lane * 16));
 }
 
-__device__ inline int pack4_fp8(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-}
-
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fp8_kernel(Plan p, int total, const uint8_t *__restrict__ q8,
@@ -220,7 +215,7 @@ void attn_fp8_kernel(Plan p, int total, const uint8_t *__restrict__ q8,
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         pv[t] = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + t], scale_log2, -m_use));
-      pf[j] = pack4_fp8(pv[0], pv[1], pv[2], pv[3]);
+      pf[j] = (int)fp8_pack4(pv[0], pv[1], pv[2], pv[3]);
     }
     lsum = mfma8(ones, pf, lsum, kOne, kOne);
 #pragma unroll

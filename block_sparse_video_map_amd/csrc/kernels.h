@@ -7,9 +7,11 @@
 #include "plan.h"
 
 hipError_t launch_build_map(const Plan &p, int32_t *s2t, hipStream_t stream);
+// q8/k8/v8/scales non-null (bf16 only): also the E4M3 copies and scale bytes
+// that launch_quant_fp8 would write, from the same pass.
 hipError_t launch_gather(const Plan &p, const void *q, const void *k, const void *v,
-                         const int32_t *s2t, void *qt, void *kt, void *vt,
-                         hipStream_t stream);
+                         const int32_t *s2t, void *qt, void *kt, void *vt, uint8_t *q8,
+                         uint8_t *k8, uint8_t *v8, uint8_t *scales, hipStream_t stream);
 // Tiles to pool: per (batch*head), tiles tile0 .. tile0+ntiles-1 of the tiled
 // copies (ntiles < 0: the head's video tiles); source z of the launch reads
 // src[z] with weights w[z] and writes rows ((z*B*H + bh)*rows + i) of the

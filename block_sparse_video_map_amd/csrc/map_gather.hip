@@ -3,8 +3,11 @@
 // One workgroup per (tile, batch*head, tensor). The tile's 64 rows are read
 // once with 16-byte coalesced loads into LDS (pads become zero rows), then
 // written out in the tiled operand layout as contiguous 16-byte vectors, so
-// both the HBM reads and the HBM writes are full-width.
+// both the HBM reads and the HBM writes are full-width. For the fp8 path the
+// same pass also writes the tile's E4M3 copy and scale byte from LDS (the
+// quantizer's rule), so the bf16 tiles are not read back.
 #include "device_common.h"
+#include "fp8_layout.h"
 #include "kernels.h"
 
 namespace vsa {
@@ -27,11 +30,14 @@ __global__ __launch_bounds__(256) void gather_kernel(Plan p, const T *__restrict
                                                      const T *__restrict__ v,
                                                      const int32_t *__restrict__ s2t,
                                                      T *__restrict__ qt, T *__restrict__ kt,
-                                                     T *__restrict__ vt) {
+                                                     T *__restrict__ vt, uint8_t *q8,
+                                                     uint8_t *k8, uint8_t *v8,
+                                                     uint8_t *scales) {
   constexpr int EPC = 16 / sizeof(T);    // elements per 16-byte chunk
   constexpr int CPR = D / EPC;           // chunks per row
   constexpr int LD = D + EPC;            // padded LDS row (keeps 16 B alignment)
   __shared__ __attribute__((aligned(16))) T tile_lds[kTile * LD];
+  __shared__ float red[4];
 
   const int tile = blockIdx.x;
   const int bh = blockIdx.y;
@@ -43,14 +49,22 @@ __global__ __launch_bounds__(256) void gather_kernel(Plan p, const T *__restrict
   T *dst = which == 0 ? qt : which == 1 ? kt : vt;
   if (!src) return;
 
+  const bool fp8 = sizeof(T) == 2 && q8 != nullptr;      // uniform over the launch
   const int32_t *map = s2t + ((int64_t)s * p.max_tiles + tile) * kTile;
   const T *src_bh = src + (int64_t)bh * p.N * D;
+  float amax = 0.f;
   for (int i = threadIdx.x; i < kTile * CPR; i += blockDim.x) {
     int row = i / CPR, cc = i % CPR;
     int32_t tok = map[row];
     uint4 val = make_uint4(0, 0, 0, 0);
     if (tok >= 0) val = *reinterpret_cast<const uint4 *>(src_bh + (int64_t)tok * D + cc * EPC);
     *reinterpret_cast<uint4 *>(&tile_lds[row * LD + cc * EPC]) = val;
+    if (fp8) {
+      const uint32_t w[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        amax = fmaxf(amax, fabsf(bf16_to_float((bf16_bits)(w[j / 2] >> (16 * (j % 2))))));
+    }
   }
   __syncthreads();
 
@@ -80,15 +94,26 @@ __global__ __launch_bounds__(256) void gather_kernel(Plan p, const T *__restrict
       reinterpret_cast<uint4 *>(out + vec * 8)[1] = reinterpret_cast<uint4 *>(e8)[1];
     }
   }
+  if constexpr (sizeof(T) == 2) {
+    if (fp8) {
+      const int e = fp8_tile_exponent(block_amax(amax, red, 256));
+      uint8_t *dst8 = (which == 0 ? q8 : which == 1 ? k8 : v8) +
+                      ((int64_t)bh * p.max_tiles + tile) * (kTile * D);
+      fp8_write_tile<D, LD>(tile_lds, col, e, dst8, 256);
+      if (threadIdx.x == 0)
+        scales[((int64_t)bh * p.max_tiles + tile) * 4 + which] = (uint8_t)(e + kFp8ExpBias);
+    }
+  }
 }
 
 template <typename T, int D>
 hipError_t gather_t(const Plan &p, const void *q, const void *k, const void *v,
-                    const int32_t *s2t, void *qt, void *kt, void *vt, hipStream_t st) {
+                    const int32_t *s2t, void *qt, void *kt, void *vt, uint8_t *q8,
+                    uint8_t *k8, uint8_t *v8, uint8_t *scales, hipStream_t st) {
   dim3 grid(p.max_tiles, p.B * p.H, 3);
   hipLaunchKernelGGL((gather_kernel<T, D>), grid, dim3(256), 0, st, p,
                      (const T *)q, (const T *)k, (const T *)v, s2t, (T *)qt, (T *)kt,
-                     (T *)vt);
+                     (T *)vt, q8, k8, v8, scales);
   return hipGetLastError();
 }
 
@@ -103,12 +128,18 @@ hipError_t launch_build_map(const Plan &p, int32_t *s2t, hipStream_t stream) {
 }
 
 hipError_t launch_gather(const Plan &p, const void *q, const void *k, const void *v,
-                         const int32_t *s2t, void *qt, void *kt, void *vt,
-                         hipStream_t stream) {
+                         const int32_t *s2t, void *qt, void *kt, void *vt, uint8_t *q8,
+                         uint8_t *k8, uint8_t *v8, uint8_t *scales, hipStream_t stream) {
   if (p.dtype == VSA_BF16) {
-    if (p.d == 128) return vsa::gather_t<bf16_bits, 128>(p, q, k, v, s2t, qt, kt, vt, stream);
-    return vsa::gather_t<bf16_bits, 64>(p, q, k, v, s2t, qt, kt, vt, stream);
+    if (p.d == 128)
+      return vsa::gather_t<bf16_bits, 128>(p, q, k, v, s2t, qt, kt, vt, q8, k8, v8, scales,
+                                           stream);
+    return vsa::gather_t<bf16_bits, 64>(p, q, k, v, s2t, qt, kt, vt, q8, k8, v8, scales,
+                                        stream);
   }
-  if (p.d == 128) return vsa::gather_t<float, 128>(p, q, k, v, s2t, qt, kt, vt, stream);
-  return vsa::gather_t<float, 64>(p, q, k, v, s2t, qt, kt, vt, stream);
+  if (p.d == 128)
+    return vsa::gather_t<float, 128>(p, q, k, v, s2t, qt, kt, vt, nullptr, nullptr, nullptr,
+                                     nullptr, stream);
+  return vsa::gather_t<float, 64>(p, q, k, v, s2t, qt, kt, vt, nullptr, nullptr, nullptr,
+                                  nullptr, stream);
 }

@@ -9,7 +9,9 @@
 //
 // One workgroup per (tile, batch*head, tensor): the tile is unpacked into
 // LDS in plain slot-major order while its largest |x| is reduced, then every
-// thread packs 16-byte chunks of the output layout from LDS.
+// thread packs 16-byte chunks of the output layout from LDS. The gather can
+// do the same in its own pass (launch_gather with fp8 outputs); this kernel
+// serves tiles that are already gathered.
 #include "device_common.h"
 #include "fp8_layout.h"
 #include "kernels.h"
@@ -18,12 +20,6 @@ namespace vsa {
 namespace {
 
 constexpr int kQThreads = 256;
-
-__device__ inline uint32_t pack4_fp8(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);     // bytes 0, 1
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);          // bytes 2, 3
-  return (uint32_t)w;
-}
 
 template <int D>
 __global__ __launch_bounds__(kQThreads) void quant_fp8_kernel(
@@ -56,50 +52,8 @@ __global__ __launch_bounds__(kQThreads) void quant_fp8_kernel(
       amax = fmaxf(amax, fabsf(bf16_to_float(u)));
     }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-  if (threadIdx.x % 64 == 0) wmax[threadIdx.x / 64] = amax;
-  __syncthreads();
-  amax = wmax[0];
-#pragma unroll
-  for (int w = 1; w < kQThreads / 64; ++w) amax = fmaxf(amax, wmax[w]);
-
-  // amax = m * 2^E, 0.5 <= m < 1, and 448 = 0.875 * 2^9.
-  int e = 0;
-  if (amax > 0.f) {
-    int E;
-    const float m = frexpf(amax, &E);
-    e = m <= 0.875f ? E - 9 : E - 8;
-    e = e < -kFp8ExpBias ? -kFp8ExpBias : e;
-  }
-
-  // Output chunk ch = bytes 16*ch .. 16*ch+15 = block ch/128, half (ch/64)%2,
-  // lane ch%64 of the fp8 layout.
-  for (int ch = threadIdx.x; ch < kTile * D / 16; ch += kQThreads) {
-    const int blk = ch / 128, half = (ch / 64) % 2, lane = ch % 64, g = lane / 32;
-    float x[16];
-    if (which == 2) {
-      const int c = blk * 32 + lane % 32;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int key = half * 32 + 8 * (j / 4) + 4 * g + j % 4;
-        x[j] = bf16_to_float(xs[key * LD + c]);
-      }
-    } else {
-      const int slot = (blk / (D / 64)) * 32 + lane % 32;
-      const int c0 = (blk % (D / 64)) * 64 + 32 * g + 16 * half;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) x[j] = bf16_to_float(xs[slot * LD + c0 + j]);
-    }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) x[j] = ldexpf(x[j], -e);    // exact: a power of two
-    uint4 o;
-    o.x = pack4_fp8(x[0], x[1], x[2], x[3]);
-    o.y = pack4_fp8(x[4], x[5], x[6], x[7]);
-    o.z = pack4_fp8(x[8], x[9], x[10], x[11]);
-    o.w = pack4_fp8(x[12], x[13], x[14], x[15]);
-    *reinterpret_cast<uint4 *>(dst + ch * 16) = o;
-  }
+  const int e = fp8_tile_exponent(block_amax(amax, wmax, kQThreads));
+  fp8_write_tile<D, LD>(xs, which == 2, e, dst, kQThreads);
   if (threadIdx.x == 0)
     exps[((int64_t)bh * p.max_tiles + tile) * 4 + which] = (uint8_t)(e + kFp8ExpBias);
 }

@@ -31,7 +31,7 @@ EXPORTS = ("vsa_query_sizes", "vsa_pooled_bytes", "vsa_map_tiles", "vsa_tile_sco
            "vsa_select_topk", "vsa_sparse_attn_fwd", "vsa_kept_stats",
            "vsa_count_flops", "vsa_ref_sizes", "vsa_ref_pooled_bytes", "vsa_ref_scores",
            "vsa_ref_select", "vsa_sparse_attn_fwd_ref", "vsa_kept_stats_ref",
-           "vsa_count_flops_ref", "vsa_teacher_map", "vsa_quantize_fp8",
+           "vsa_count_flops_ref", "vsa_teacher_map", "vsa_quantize_fp8", "vsa_map_tiles_fp8",
            "vsa_sparse_attn_fwd_fp8", "vsa_status_string", "vsa_version")
 
 
@@ -102,6 +102,7 @@ def lib() -> ctypes.CDLL:
             "vsa_count_flops_ref": [P, f64, R, vp, vp, vp, ctypes.POINTER(f64)],
             "vsa_teacher_map": [P, vp, vp, vp, f32, vp, vp, vp],
             "vsa_quantize_fp8": [P, vp, vp, vp, vp, vp, vp, vp, vp],
+            "vsa_map_tiles_fp8": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "vsa_sparse_attn_fwd_fp8": [P, vp, vp, vp, vp, vp, vp, f64, R, vp, f32, vp, vp, vp],
             "vsa_status_string": [ctypes.c_int],
             "vsa_version": [],
@@ -419,6 +420,25 @@ def vsa_quantize_fp8(prob: Problem, qt, kt, vt, q8, k8, v8, scales, stream=None)
         _stream(stream)))
 
 
+def vsa_map_tiles_fp8(prob: Problem, q, k, v, slot_to_token, qt, kt, vt, q8, k8, v8, scales,
+                      stream=None):
+    """vsa_map_tiles plus the E4M3 copies and scale bytes, in one pass."""
+    import torch
+    sz = vsa_query_sizes(prob, 0.0)
+    et = _elem_dtype(prob)
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _need(x, sz.out_elems, et, name)
+    for name, x in (("qt", qt), ("kt", kt), ("vt", vt)):
+        _need(x, sz.tiled_elems, et, name)
+    for name, x in (("q8", q8), ("k8", k8), ("v8", v8)):
+        _need(x, sz.tiled_elems, torch.uint8, name)
+    _need(slot_to_token, sz.map_elems, torch.int32, "slot_to_token")
+    _need(scales, fp8_scale_bytes(prob), torch.uint8, "scales")
+    _check("vsa_map_tiles_fp8", lib().vsa_map_tiles_fp8(
+        prob.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(slot_to_token), _ptr(qt), _ptr(kt), _ptr(vt),
+        _ptr(q8), _ptr(k8), _ptr(v8), _ptr(scales), _stream(stream)))
+
+
 def vsa_sparse_attn_fwd_fp8(prob: Problem, q8, k8, v8, scales, slot_to_token, kv_idx,
                             sparsity: float, softmax_scale: float, out, lse=None,
                             budget: Optional[vsa_ref_budget] = None, ref_idx=None,
@@ -490,6 +510,10 @@ class Layer:
     def map_tiles(self, q, k, v, stream=None):
         vsa_map_tiles(self.prob, q, k, v, self.slot_to_token, self.qt, self.kt, self.vt, stream)
 
+    def map_tiles_fp8(self, q, k, v, stream=None):
+        vsa_map_tiles_fp8(self.prob, q, k, v, self.slot_to_token, self.qt, self.kt, self.vt,
+                          self.q8, self.k8, self.v8, self.fp8_scales, stream)
+
     def quantize(self, stream=None):
         vsa_quantize_fp8(self.prob, self.qt, self.kt, self.vt, self.q8, self.k8, self.v8,
                          self.fp8_scales, stream)
@@ -529,10 +553,12 @@ class Layer:
                             softmax_scale, self.out, self.lse, stream)
 
     def forward(self, q, k, v, wq, wk, softmax_scale: float = 0.0, stream=None):
-        """One whole layer: map+gather, scores, top-k, attention."""
-        self.map_tiles(q, k, v, stream)
+        """One whole layer: map+gather, scores, top-k, attention (fp8: the
+        gather also writes the E4M3 tiles)."""
         if self.fp8:
-            self.quantize(stream)
+            self.map_tiles_fp8(q, k, v, stream)
+        else:
+            self.map_tiles(q, k, v, stream)
         if self.sparsity != 0.0:
             self.tile_scores(wq, wk, stream)
             self.select(stream)

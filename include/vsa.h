@@ -371,6 +371,17 @@ VSA_API int vsa_quantize_fp8(const vsa_problem *prob, const void *qt, const void
                              void *stream);
 
 /*
+ * vsa_map_tiles_fp8 - vsa_map_tiles and vsa_quantize_fp8 in one pass: the
+ * same slot_to_token, bf16 tiles (for scoring) and E4M3 tiles plus scale
+ * bytes (for vsa_sparse_attn_fwd_fp8), bit for bit, without reading the
+ * bf16 tiles back. q, k, v and every output are required; bf16 only.
+ */
+VSA_API int vsa_map_tiles_fp8(const vsa_problem *prob, const void *q, const void *k,
+                              const void *v, int32_t *slot_to_token, void *qt, void *kt,
+                              void *vt, void *q8, void *k8, void *v8, void *scales,
+                              void *stream);
+
+/*
  * vsa_sparse_attn_fwd_fp8 - step 4 on the fp8 copies: the same key-tile
  * lists, mask and outputs as vsa_sparse_attn_fwd (budget == NULL) or
  * vsa_sparse_attn_fwd_ref (budget and ref_idx given), computed from the E4M3

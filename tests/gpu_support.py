@@ -113,6 +113,15 @@ def to_device(w: Workload, heads=None, arrays=None):
     return t
 
 
+def make_qkv_f32(w: Workload):
+    """The workload's seeded Q, K, V as float32 [B, H, N, d] (bf16-exact for
+    bf16 workloads)."""
+    q, k, v = make_qkv(w, as_bf16_bits=(w.dtype == "bf16"))
+    if w.dtype == "bf16":
+        return tuple(bf16_to_f32(x) for x in (q, k, v))
+    return q, k, v
+
+
 def problem_of(w: Workload, H=None):
     from block_sparse_video_map_amd import vsa
     return vsa.Problem(w.B, w.H if H is None else H, w.d, w.grid, w.prefix, w.tile_shapes,

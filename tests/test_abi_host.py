@@ -336,3 +336,22 @@ def test_fp8_scale_bytes():
     p = _problem(w)
     sz = vsa.vsa_query_sizes(p, w.sparsity)
     assert vsa.fp8_scale_bytes(p) == w.B * w.H * sz.max_tiles * 4
+
+
+def test_fused_map_fp8_rejects_before_any_launch():
+    L = vsa.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    w = WORKLOADS["1"]
+    assert L.vsa_map_tiles_fp8(_problem(w).ref, *([fake] * 11), None) == vsa.VSA_ERR_UNSUPPORTED
+    pb = _problem(w, dtype="bf16")
+    args = [fake] * 11
+    for i in range(11):                        # every buffer is required
+        a = list(args)
+        a[i] = None
+        assert L.vsa_map_tiles_fp8(pb.ref, *a, None) == vsa.VSA_ERR_INVALID_ARG
+    a = list(args)
+    a[10] = ctypes.c_void_p((1 << 20) + 2)      # scales not 4-byte aligned
+    assert L.vsa_map_tiles_fp8(pb.ref, *a, None) == vsa.VSA_ERR_INVALID_ARG
+    a = list(args)
+    a[7] = ctypes.c_void_p((1 << 20) + 8)       # q8 not 16-byte aligned
+    assert L.vsa_map_tiles_fp8(pb.ref, *a, None) == vsa.VSA_ERR_INVALID_ARG

@@ -106,6 +106,83 @@ def test_fp8_attention_parity(name):
             _compare(w, layer, b, h, allow, tm)
 
 
+def _extreme_arrays(w, tm):
+    """Seeded inputs with tiles that take every branch of the scale rule: all
+    zero (e = 0), bf16 subnormals (e clamped to -127), values near the bf16
+    maximum (e = 120), and amax exactly 448 * 2^5 (e = 5, no rounding)."""
+    from workloads.inputs import bf16_to_f32, bf16_bits
+    q, k, v = (np.asarray(a, dtype=np.float32).copy() for a in gs.make_qkv_f32(w))
+    npf = tm.n_prefix_tiles
+    special = {npf + 0: 0.0, npf + 1: 2.0 ** -130, npf + 2: 3.0e38, npf + 3: 448.0 * 2.0 ** 5}
+    rng = np.random.default_rng(9)
+    for x in (q, k, v):
+        for tile, amp in special.items():
+            toks = tm.tile_tokens(tile)
+            vals = rng.uniform(-1.0, 1.0, (x.shape[0], x.shape[1], toks.size, w.d)) * amp
+            if amp in (448.0 * 2.0 ** 5, 3.0e38):
+                vals[..., 0, 0] = amp                      # fixes the tile's amax
+            x[:, :, toks, :] = vals
+    return [bf16_to_f32(bf16_bits(a)) for a in (q, k, v)]
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["quantizer", "fused-gather"])
+def test_quantize_fp8_extreme_tiles(fused):
+    import torch
+    from block_sparse_video_map_amd import vsa
+    w = SMALL["mg-d64"]
+    tm = oracle.tile_map(*w.grid, w.prefix, w.tile_shapes[0])
+    npf = tm.n_prefix_tiles
+    arrays = _extreme_arrays(w, tm)
+    layer = vsa.Layer(gs.problem_of(w), w.sparsity, vsa.VSA_SCORE_MEAN_GATE, w.d, fp8=True)
+    dq, dk, dv = gs.to_device(w, arrays=arrays)
+    if fused:
+        layer.map_tiles_fp8(dq, dk, dv)
+    else:
+        layer.map_tiles(dq, dk, dv)
+        layer.quantize()
+    torch.cuda.synchronize()
+    sz = layer.sizes
+    per_head = sz.max_tiles * 64 * w.d
+    exps = layer.fp8_scales.cpu().numpy().reshape(w.B * w.H, sz.max_tiles, 4).astype(np.int64)
+    exps -= 127
+    for h in range(w.H):
+        for which, (x, t) in enumerate(zip(arrays, (layer.q8, layer.k8, layer.v8))):
+            want, we = oracle.quantize_tiles_e4m3(oracle.gather(x[0, h].astype(np.float64), tm))
+            got_e = exps[h, :tm.n_tiles, which]
+            np.testing.assert_array_equal(got_e, we)
+            assert got_e[npf] == 0 and got_e[npf + 1] == -127 and got_e[npf + 2] == 120
+            assert got_e[npf + 3] == 5
+            codes = t[h * per_head:(h + 1) * per_head].cpu().numpy()
+            got = gs.unpack_fp8_tiles(codes, exps[h, :, which], tm.n_tiles, w.d, col=(which == 2))
+            np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("name", ["tp-d128", "mg-d64"])
+def test_fused_gather_matches_map_then_quantize(name):
+    """vsa_map_tiles_fp8 writes exactly what vsa_map_tiles followed by
+    vsa_quantize_fp8 writes: map, bf16 tiles, E4M3 tiles and scale bytes."""
+    import torch
+    from block_sparse_video_map_amd import vsa
+    w = SMALL[name]
+    layer = vsa.Layer(gs.problem_of(w), w.sparsity, vsa.score_mode(w.scorer, w.tripool_mode),
+                      w.d if w.scorer == "mean_gate" else w.proj_dim, fp8=True)
+    dq, dk, dv = gs.to_device(w)
+    bufs = (layer.slot_to_token, layer.qt, layer.kt, layer.vt, layer.q8, layer.k8, layer.v8,
+            layer.fp8_scales)
+    for t in bufs:
+        t.zero_()
+    layer.map_tiles(dq, dk, dv)
+    layer.quantize()
+    torch.cuda.synchronize()
+    first = [t.clone() for t in bufs]
+    for t in bufs:
+        t.zero_()
+    layer.map_tiles_fp8(dq, dk, dv)
+    torch.cuda.synchronize()
+    for a, b in zip(first, bufs):
+        assert torch.equal(a, b)
+
+
 def test_fp8_dense_path():
     """sparsity 0: every tile kept, dense attention over the E4M3 inputs."""
     w = SMALL["mg-d64"]
