@@ -25,6 +25,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 HBM_PEAK_GBS = 8000.0
 
 
@@ -349,10 +350,15 @@ def main():
                        "effective_tflops_attention": f / mn2["attention"] / 1e9,
                        "effective_tflop": f / 1e12, "stage_ms_median": m2}
         if fp8:
+            from block_sparse_video_map_amd.profsum import read_traffic
             extra[name]["precision"] = ("E4M3 Q/K/V and probabilities, fp32 accumulation, "
                                         "bf16 output: a reduced-precision variant, not the "
                                         "headline")
-            extra[name]["frac_of_fp8_peak"] = round(f / mn2["attention"] / 1e9 / 5000.0, 4)
+            extra[name]["frac_of_fp8_peak"] = round(f / mn2["attention"] / 1e9 / FP8_PEAK_TFLOPS,
+                                                    4)
+            rec = read_traffic(os.path.join(ROOT, "profiles", f"attn_fp8_{name[:-4]}_traffic.md"),
+                               "attn_fp8_kernel", name[:-4]) if heads is None else None
+            extra[name]["traffic"] = rec["bytes_per_launch"] if rec else None
         c.release()
         log(f"[bench] {name}: {ms:.3f} ms/step")
 

@@ -25,13 +25,17 @@ import re
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-# Sources whose text decides the attention kernel's memory traffic.
-ATTN_SOURCES = ("csrc/attn_bf16.hip", "csrc/attn_common.h", "csrc/device_common.h")
+# Sources whose text decides each attention kernel's memory traffic.
+KERNEL_SOURCES = {
+    "attn_bf16_kernel": ("csrc/attn_bf16.hip", "csrc/attn_common.h", "csrc/device_common.h"),
+    "attn_fp8_kernel": ("csrc/attn_fp8.hip", "csrc/attn_common.h", "csrc/device_common.h",
+                        "csrc/fp8_layout.h"),
+}
 
 
-def source_hash(files=ATTN_SOURCES) -> str:
+def source_hash(kernel: str = "attn_bf16_kernel") -> str:
     h = hashlib.sha256()
-    for f in files:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(PKG, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -162,7 +166,7 @@ def main(argv=None):
                "bytes_per_launch": round(r["bytes_per_launch"]),
                "fetch_bytes": round(r["fetch_bytes"]), "write_bytes": round(r["write_bytes"]),
                "fetch_scale": round(r["fetch_scale"], 5), "write_scale": round(r["write_scale"], 5),
-               "source_hash": source_hash()}
+               "source_hash": source_hash(a.kernel)}
         lines.append(f"<!-- traffic: {json.dumps(rec)} -->")
     sys.stdout.write("\n".join(lines) + "\n")
 
@@ -181,7 +185,7 @@ def read_traffic(path: str, kernel: str, workload: str):
     rec = json.loads(m.group(1))
     if rec.get("kernel") != kernel or rec.get("workload") != workload:
         return None
-    if rec.get("source_hash") != source_hash():
+    if kernel not in KERNEL_SOURCES or rec.get("source_hash") != source_hash(kernel):
         return None
     return rec
 

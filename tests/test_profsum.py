@@ -30,6 +30,15 @@ def test_stale_or_foreign_summary_is_ignored(tmp_path):
     assert profsum.read_traffic(str(tmp_path / "missing.md"), "attn_bf16_kernel", "3a") is None
 
 
+def test_hash_is_per_kernel(tmp_path):
+    assert profsum.source_hash("attn_bf16_kernel") != profsum.source_hash("attn_fp8_kernel")
+    p = _summary(tmp_path, kernel="attn_fp8_kernel",
+                 source_hash=profsum.source_hash("attn_fp8_kernel"))
+    assert profsum.read_traffic(p, "attn_fp8_kernel", "3a")["bytes_per_launch"] == 123
+    p = _summary(tmp_path, kernel="attn_fp8_kernel")      # bf16 sources' hash
+    assert profsum.read_traffic(p, "attn_fp8_kernel", "3a") is None
+
+
 def test_short_kernel_names():
     assert profsum.short_name("vsa::(anonymous namespace)::scores_kernel(Plan, int)") == \
         "scores_kernel"
