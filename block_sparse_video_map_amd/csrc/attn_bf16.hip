@@ -13,9 +13,12 @@
 // ("unit") of a tile is copied from HBM straight into a two-slot LDS ring of
 // the split by direct-to-LDS buffer loads (wave 0 copies the K blocks, wave
 // 1 the V blocks; no registers held while in flight), one unit ahead of its
-// use. One workgroup barrier per unit orders "next slot landed" and "this
-// slot read by both waves". With two waves per SIMD the hardware overlaps
-// one wave's softmax (VALU) with the other's products (MFMA).
+// use. Only the two waves of a split wait for each other, once per unit,
+// through a pair of LDS counters ("next slot landed", "this slot read by
+// both"); the four splits drift freely, so on each SIMD one split's softmax
+// (VALU) tends to overlap another split's products (MFMA). A workgroup-wide
+// barrier per unit instead keeps all eight waves in step and measured 3.7%
+// slower.
 //
 // The products are taken transposed, S^T = K Q^T and O^T = V^T P^T, so that
 // every lane owns one query column: the S^T accumulator is already the B
@@ -71,6 +74,7 @@ void attn_bf16_kernel(Plan p, int total, const bf16_bits *__restrict__ qt,
   // read while the other one is being filled.
   __shared__ __attribute__((aligned(1024))) bf16_bits ring0_all[kSplits * 2 * UNIT];
   __shared__ __attribute__((aligned(1024))) bf16_bits ring1_all[kSplits * 2 * UNIT];
+  __shared__ int pair_count[kSplits * 2];      // units finished, per (split, wave)
 
   int b, h, tq;
   work_item(p, total, b, h, tq);
@@ -223,28 +227,38 @@ void attn_bf16_kernel(Plan p, int total, const bf16_bits *__restrict__ qt,
     }
   };
 
-  // Unit 2i + kb is key half kb of the row's i-th tile; even units use slot
+  // Wait for the other wave of this split to finish its n-th unit, after
+  // posting our own: own copies landed and own reads of the old slot done
+  // (all counters drained) before the post. The wait is bounded, so it ends
+  // even if the partner never posts (which the schedule below rules out).
+  typedef volatile __attribute__((address_space(3))) int *lds_iptr;
+  const lds_iptr count = (lds_iptr)pair_count;
+  auto pair_sync = [&](int n) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    if (lane == 0) count[ks * 2 + qb] = n;
+    for (int guard = 0; count[ks * 2 + 1 - qb] < n && guard < (1 << 24); ++guard)
+      __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  };
+
+  // Unit 2i + kb is key half kb of the split's i-th tile; even units use slot
   // ring0, odd units ring1. The copy of the next unit is issued before the
-  // current one is computed.
-  // Every wave runs the same number of steps (barriers); a split with fewer
-  // tiles idles through the last step.
-  const int n_steps = (n_kv + kSplits - 1) / kSplits;
+  // current one is computed. Both waves of a split run the same n_mine steps.
   bool ok = false;
   int t = 0;
   uint64_t mask = 0;
+  if (threadIdx.x < kSplits * 2) pair_count[threadIdx.x] = 0;
   if (n_mine > 0) {
     t = tile_of(0, ok);
     mask = tile_mask(t, ok);
     issue(ring0, t, 0);
   }
   sync_slots();
-  for (int i = 0; i < n_steps; ++i) {
-    const bool mine = i < n_mine;
-    if (mine) {
-      issue(ring1, t, 1);
-      unit(ring0, (uint32_t)mask);
-    }
-    sync_slots();
+  for (int i = 0; i < n_mine; ++i) {
+    issue(ring1, t, 1);
+    unit(ring0, (uint32_t)mask);
+    pair_sync(2 * i + 1);
     const bool more = i + 1 < n_mine;
     bool ok1 = false;
     int t1 = 0;
@@ -252,14 +266,14 @@ void attn_bf16_kernel(Plan p, int total, const bf16_bits *__restrict__ qt,
       t1 = tile_of(i + 1, ok1);
       issue(ring0, t1, 0);
     }
-    if (mine) unit(ring1, (uint32_t)(mask >> 32));
-    sync_slots();
+    unit(ring1, (uint32_t)(mask >> 32));
+    pair_sync(2 * i + 2);
     t = t1;
     mask = more ? tile_mask(t1, ok1) : 0ull;
   }
+  __syncthreads();                             // every split done with its rings
 
-  // Merge the four key splits of each query half (the rings are free now:
-  // the last step ended with a barrier).
+  // Merge the four key splits of each query half (the rings are free now).
   float *osum = reinterpret_cast<float *>(ring0_all);       // [64][D], swizzled
   float *sm_m = reinterpret_cast<float *>(ring1_all);       // [kSplits][64]
   float *sm_l = sm_m + kSplits * kTile;
