@@ -35,6 +35,7 @@ __device__ inline void load_tile_f32(const T *__restrict__ src, float *xs) {
 // owning 16-column blocks w, w+4.
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 constexpr int kPoolTiles = 16;
+constexpr int kTripTiles = 8;                // TripPool: tiles per workgroup (one P load)
 
 template <typename T>
 __device__ inline void load8_f32(const T *__restrict__ src, float (&v)[8]);
@@ -148,6 +149,8 @@ __global__ __launch_bounds__(256) void pool_mean_gate_kernel(
 
 // Veda TripPool: project every real token (d -> R), then the statistics the
 // mode asks for, written in the order [Avg | Max | Min] (bits 1, 2, 4 of stats).
+// A workgroup takes kTripTiles consecutive tiles of one (batch*head, Q|K) and
+// stages the head's projection in LDS once for all of them.
 // The projection X[64 tokens x D] . P[D x R] runs on the 16x16x4 f64 MFMA:
 // wave w owns tokens 16w..16w+15 and all R columns (16-column blocks). Lane
 // l reads four consecutive channels k0 + 4*(l/16) + m of its token row and of
@@ -165,94 +168,103 @@ __global__ __launch_bounds__(256) void pool_trippool_kernel(
   __shared__ double red[3][4][RB * 16];      // [stat][wave][column]
   __shared__ int valid[kTile];
 
-  const int vt_i = blockIdx.x, bh = blockIdx.y, which = blockIdx.z;
+  const int bh = blockIdx.y, which = blockIdx.z;
   const int h = bh % p.H, s = h % p.n_shapes;
-  if (vt_i >= (job.ntiles < 0 ? p.n_vt[s] : job.ntiles)) return;
-  const int tile = job.tile0 + vt_i;
-  const T *src = (const T *)job.src[which] + ((int64_t)bh * p.max_tiles + tile) * (kTile * D);
+  const int n_rows = job.ntiles < 0 ? p.n_vt[s] : job.ntiles;
+  const int first = blockIdx.x * kTripTiles;
+  if (first >= n_rows) return;
+  const int last = min(first + kTripTiles, n_rows);
   const float *w = job.w[which] + (int64_t)h * D * R;
 
-  if (threadIdx.x < kTile)
-    valid[threadIdx.x] = s2t[((int64_t)s * p.max_tiles + tile) * kTile + threadIdx.x] >= 0;
+  // The head's projection, once per workgroup: consecutive threads read
+  // consecutive columns of a row of P (coalesced), stored transposed.
   for (int i = threadIdx.x; i < RB * 16 * D; i += blockDim.x) {
-    const int c = i % D, j = i / D;          // pt[j][c] = P[c][j], zero past R
+    const int j = i % (RB * 16), c = i / (RB * 16);   // pt[j][c] = P[c][j], zero past R
     pt[j * LD + c] = j < R ? w[c * R + j] : 0.f;
   }
-  load_tile_f32<T, D, LD>(src, xs);
-  __syncthreads();
-
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
   const int lane = threadIdx.x % 64, g = lane / 16, l16 = lane % 16;
-  f64x4 acc[RB];
+
+  for (int vt_i = first; vt_i < last; ++vt_i) {
+    const int tile = job.tile0 + vt_i;
+    const T *src = (const T *)job.src[which] + ((int64_t)bh * p.max_tiles + tile) * (kTile * D);
+    __syncthreads();                         // the previous tile's LDS reads are done
+    if (threadIdx.x < kTile)
+      valid[threadIdx.x] = s2t[((int64_t)s * p.max_tiles + tile) * kTile + threadIdx.x] >= 0;
+    load_tile_f32<T, D, LD>(src, xs);
+    __syncthreads();
+
+    f64x4 acc[RB];
 #pragma unroll
-  for (int b = 0; b < RB; ++b) acc[b] = (f64x4){0.0, 0.0, 0.0, 0.0};
-  const float *xrow = xs + (wave * 16 + l16) * LD;
+    for (int b = 0; b < RB; ++b) acc[b] = (f64x4){0.0, 0.0, 0.0, 0.0};
+    const float *xrow = xs + (wave * 16 + l16) * LD;
 #pragma unroll 2
-  for (int k0 = 0; k0 < D; k0 += 16) {
-    const int kk = k0 + 4 * g;
-    const float4 xa = *reinterpret_cast<const float4 *>(xrow + kk);
-    const double a4[4] = {xa.x, xa.y, xa.z, xa.w};
-    double b4[RB][4];
+    for (int k0 = 0; k0 < D; k0 += 16) {
+      const int kk = k0 + 4 * g;
+      const float4 xa = *reinterpret_cast<const float4 *>(xrow + kk);
+      const double a4[4] = {xa.x, xa.y, xa.z, xa.w};
+      double b4[RB][4];
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        const float4 pb = *reinterpret_cast<const float4 *>(pt + (b * 16 + l16) * LD + kk);
+        b4[b][0] = pb.x; b4[b][1] = pb.y; b4[b][2] = pb.z; b4[b][3] = pb.w;
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int b = 0; b < RB; ++b)
+          acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(a4[m], b4[b][m], acc[b], 0, 0, 0);
+    }
+
+    // Element e of lane l: token wave*16 + 4e + l/16, column b*16 + l%16.
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
-      const float4 pb = *reinterpret_cast<const float4 *>(pt + (b * 16 + l16) * LD + kk);
-      b4[b][0] = pb.x; b4[b][1] = pb.y; b4[b][2] = pb.z; b4[b][3] = pb.w;
-    }
+      double sum = 0.0, mx = -INFINITY, mn = INFINITY;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+      for (int e = 0; e < 4; ++e) {
+        if (valid[wave * 16 + 4 * e + g]) {
+          sum += acc[b][e];
+          mx = fmax(mx, acc[b][e]);
+          mn = fmin(mn, acc[b][e]);
+        }
+      }
 #pragma unroll
-      for (int b = 0; b < RB; ++b)
-        acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(a4[m], b4[b][m], acc[b], 0, 0, 0);
-  }
-
-  // Element e of lane l: token wave*16 + 4e + l/16, column b*16 + l%16.
-#pragma unroll
-  for (int b = 0; b < RB; ++b) {
-    double sum = 0.0, mx = -INFINITY, mn = INFINITY;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (valid[wave * 16 + 4 * e + g]) {
-        sum += acc[b][e];
-        mx = fmax(mx, acc[b][e]);
-        mn = fmin(mn, acc[b][e]);
+      for (int d = 16; d < 64; d <<= 1) {    // the four lanes of a column
+        sum += __shfl_xor(sum, d);
+        mx = fmax(mx, __shfl_xor(mx, d));
+        mn = fmin(mn, __shfl_xor(mn, d));
+      }
+      if (g == 0) {
+        red[0][wave][b * 16 + l16] = sum;
+        red[1][wave][b * 16 + l16] = mx;
+        red[2][wave][b * 16 + l16] = mn;
       }
     }
-#pragma unroll
-    for (int d = 16; d < 64; d <<= 1) {      // the four lanes of a column
-      sum += __shfl_xor(sum, d);
-      mx = fmax(mx, __shfl_xor(mx, d));
-      mn = fmin(mn, __shfl_xor(mn, d));
-    }
-    if (g == 0) {
-      red[0][wave][b * 16 + l16] = sum;
-      red[1][wave][b * 16 + l16] = mx;
-      red[2][wave][b * 16 + l16] = mn;
-    }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  if (threadIdx.x < R) {
-    const int j = threadIdx.x;
-    int n = 0;
-    for (int sl = 0; sl < kTile; ++sl) n += valid[sl];
-    double ts = 0.0, tx = -INFINITY, tn = INFINITY;
+    if (threadIdx.x < R) {
+      const int j = threadIdx.x;
+      int n = 0;
+      for (int sl = 0; sl < kTile; ++sl) n += valid[sl];
+      double ts = 0.0, tx = -INFINITY, tn = INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-      ts += red[0][ww][j];
-      tx = fmax(tx, red[1][ww][j]);
-      tn = fmin(tn, red[2][ww][j]);
+      for (int ww = 0; ww < 4; ++ww) {
+        ts += red[0][ww][j];
+        tx = fmax(tx, red[1][ww][j]);
+        tn = fmin(tn, red[2][ww][j]);
+      }
+      const int width = __builtin_popcount(stats) * R;
+      double *out = pooled + (((int64_t)which * p.B * p.H + bh) * job.rows + vt_i) * width + j;
+      if (stats & 1) {
+        *out = ts / (double)n;
+        out += R;
+      }
+      if (stats & 2) {
+        *out = tx;
+        out += R;
+      }
+      if (stats & 4) *out = tn;
     }
-    const int width = __builtin_popcount(stats) * R;
-    double *out = pooled + (((int64_t)which * p.B * p.H + bh) * job.rows + vt_i) * width + j;
-    if (stats & 1) {
-      *out = ts / (double)n;
-      out += R;
-    }
-    if (stats & 2) {
-      *out = tx;
-      out += R;
-    }
-    if (stats & 4) *out = tn;
   }
 }
 
@@ -356,7 +368,7 @@ template <typename T, int D>
 hipError_t pool_t(const Plan &p, int mode, int R, const PoolJob &job, int nsrc,
                   const int32_t *s2t, double *pooled, hipStream_t st) {
   const int rows = job.ntiles < 0 ? p.max_vt : job.ntiles;
-  dim3 grid(rows, p.B * p.H, nsrc);
+  dim3 grid((rows + kTripTiles - 1) / kTripTiles, p.B * p.H, nsrc);
   if (mode == VSA_SCORE_MEAN_GATE) {
     dim3 grid_mg((rows + kPoolTiles - 1) / kPoolTiles, p.B * p.H, nsrc);
     hipLaunchKernelGGL((pool_mean_gate_kernel<T, D>), grid_mg, dim3(256), 0, st, p, job, s2t,
