@@ -2,12 +2,17 @@
 //
 // One workgroup per score row. Scores become order-preserving 32-bit keys
 // (larger key = larger score, -0.0 folded into +0.0) held in registers, each
-// thread owning a contiguous run of indices. A most-significant-digit radix
-// select (four 8-bit passes with LDS histograms) finds the k-th largest key T
-// and how many keys equal to T are kept; ties keep the lowest indices. A
-// single ordered pass then flags "key > T, or key == T among the first ties"
-// and compacts the flagged indices with block prefix sums, which yields the
-// ascending block-index list directly. O(n) work per row, exact.
+// thread owning a contiguous run of indices. A most-significant-digit select
+// over the row's own key range finds the k-th largest key T and how many keys
+// equal to T are kept; ties keep the lowest indices. Each pass splits the
+// current range [lo, hi] into at most 256 equal power-of-two bins ((key - lo)
+// >> sh), counts them in an LDS histogram and keeps the bin holding the k-th
+// largest key; starting from the row's min..max (not the top byte of the
+// key) spreads the first pass over the bins instead of piling the row into
+// the few bins its exponents share. At most five passes. A single ordered
+// pass then flags "key > T, or key == T among the first ties" and compacts
+// the flagged indices with block prefix sums, which yields the ascending
+// block-index list directly. O(n) work per row, exact.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -51,6 +56,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Plan p, SelectJob j
   __shared__ int hist[256];
   __shared__ int wave_tot[kSelWaves];
   __shared__ int sel_bin, sel_above;
+  __shared__ uint32_t wave_lo[kSelWaves], wave_hi[kSelWaves];
 
   const int i = blockIdx.x, bh = blockIdx.y, h = bh % p.H, s = h % p.n_shapes;
   if (i >= p.n_vt[s]) return;                   // one row per video query tile
@@ -64,16 +70,41 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Plan p, SelectJob j
 #pragma unroll
   for (int e = 0; e < E; ++e) key[e] = (j0 + e < n) ? order_key(row[j0 + e]) : 0u;
 
-  // Radix select of the k-th largest key: prefix/need narrow digit by digit.
-  uint32_t prefix = 0, pmask = 0;
+  // The row's key range.
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (j0 + e < n) {
+      lo = min(lo, key[e]);
+      hi = max(hi, key[e]);
+    }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
+  }
+  if (t % 64 == 0) {
+    wave_lo[t / 64] = lo;
+    wave_hi[t / 64] = hi;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    lo = min(lo, wave_lo[w]);
+    hi = max(hi, wave_hi[w]);
+  }
+
+  // Narrow [lo, hi] to the k-th largest key; need = how many keys equal to
+  // it are kept. Each pass leaves a range below 2^sh, so sh drops by 8.
   int need = k;
 #pragma unroll 1
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  for (int pass = 0; pass < 6 && lo < hi; ++pass) {
+    const int sh = max(0, 24 - (int)__clz(hi - lo));        // bit length - 8
     hist[t] = 0;
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < E; ++e)
-      if (j0 + e < n && (key[e] & pmask) == prefix) atomicAdd(&hist[(key[e] >> shift) & 255], 1);
+      if (j0 + e < n && key[e] >= lo && key[e] <= hi) atomicAdd(&hist[(key[e] - lo) >> sh], 1);
     __syncthreads();
     // Counts from the top bin down: thread t looks at bin 255 - t.
     const int c = hist[255 - t];
@@ -85,11 +116,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(Plan p, SelectJob j
     }
     __syncthreads();
     need -= sel_above;
-    prefix |= (uint32_t)sel_bin << shift;
-    pmask |= 255u << shift;
+    const uint64_t top = (uint64_t)lo + ((uint64_t)(sel_bin + 1) << sh) - 1;
+    lo += (uint32_t)sel_bin << sh;
+    hi = top < hi ? (uint32_t)top : hi;
     __syncthreads();
   }
-  const uint32_t T = prefix;                    // k-th largest key; keep `need` ties
+  const uint32_t T = lo;                        // k-th largest key; keep `need` ties
 
   // Ordered compaction: ties are ranked by index among themselves.
   int n_eq = 0;
