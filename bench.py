@@ -289,7 +289,7 @@ def main():
     a = parse()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {a.gpus}); the path shards by head "
-              "across GPUs with no exchange, which this build does not launch.", file=sys.stderr)
+              "across GPUs with no exchange; this benchmark runs one GPU.", file=sys.stderr)
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
