@@ -189,6 +189,13 @@ void attn_bf16_kernel(Plan p, int total, const bf16_bits *__restrict__ qt,
     for (int r = 0; r < 16; ++r) sc[r] = 0.f;
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) sc = mfma32(kf[cc], qf[cc], sc);
+    __builtin_amdgcn_sched_group_barrier(0x100, NC, 0);   // the NC K fragment reads,
+    __builtin_amdgcn_sched_group_barrier(0x008, NC, 0);   // then the NC S^T products
+    // The V fragments are read now, so their LDS latency hides behind the
+    // softmax instead of stalling each PV product.
+    bf16x8 vf[2 * NDB];
+#pragma unroll
+    for (int j = 0; j < 2 * NDB; ++j) vf[j] = frag(slot + UNIT, j);
     if (mask32 != 0xFFFFFFFFu) {
       // Element r of lane (g, l32) is key (r/4)*8 + g*4 + r%4 of the unit.
 #pragma unroll
@@ -221,9 +228,8 @@ void attn_bf16_kernel(Plan p, int total, const bf16_bits *__restrict__ qt,
     l_run += ps;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const bf16x8 va = frag(slot + UNIT, db * 2), vb = frag(slot + UNIT, db * 2 + 1);
-      o[db] = mfma32(va, pf[0], o[db]);
-      o[db] = mfma32(vb, pf[1], o[db]);
+      o[db] = mfma32(vf[db * 2], pf[0], o[db]);
+      o[db] = mfma32(vf[db * 2 + 1], pf[1], o[db]);
     }
   };
 
