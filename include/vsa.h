@@ -364,7 +364,8 @@ VSA_API int vsa_teacher_map(const vsa_problem *prob, const void *qt, const void 
  * scales: device uint8 [B][H][max_tiles][4], byte 0/1/2 = e + 127 of the Q/K/V
  *   tile, byte 3 unused; 4-byte aligned.
  * Only tiles that exist for the head's shape are written. dtype must be
- * VSA_BF16 (VSA_ERR_UNSUPPORTED otherwise).
+ * VSA_BF16 (VSA_ERR_UNSUPPORTED otherwise). Inputs must be finite: a tile
+ * holding an infinity or NaN has no scale, and its codes are unspecified.
  */
 VSA_API int vsa_quantize_fp8(const vsa_problem *prob, const void *qt, const void *kt,
                              const void *vt, void *q8, void *k8, void *v8, void *scales,
