@@ -285,6 +285,44 @@ def cpu_baseline(wname: str, budget_s: float):
             "seconds": round(el, 2), "host_cpus": os.cpu_count()}
 
 
+def measured_peak(reps: int = 5) -> dict:
+    """The matrix-core rate the chip sustains under a pure MFMA load (bf16
+    and fp8), and the clocks behind it: the engine clock the runtime reports
+    (the maximum, which the published peaks assume), the clock the shader
+    tick counter shows during the load, and the effective clock that the
+    sustained bf16 rate implies at 4096 flop per clock per CU."""
+    import torch
+    from block_sparse_video_map_amd import vsa
+    cu, clk_khz, wall_khz = vsa.vsa_device_clocks()
+    n_wg = 2 * cu                                   # two waves on every SIMD
+    out = {"cus": cu, "reported_clock_ghz": clk_khz / 1e6,
+           "peak_at_reported_clock_tflops": {"bf16": cu * clk_khz * 1e3 * 4096 / 1e12,
+                                             "fp8": cu * clk_khz * 1e3 * 8192 / 1e12}}
+    ticks = torch.zeros(4 * n_wg, dtype=torch.int64, device="cuda")
+    for kind, name, iters, per_clk in ((0, "bf16", 60000, 4096), (1, "fp8", 30000, 8192)):
+        vsa.vsa_mfma_probe(kind, iters, n_wg)       # warm-up
+        ms = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            f = vsa.vsa_mfma_probe(kind, iters, n_wg, ticks)
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        t = sorted(ms)[len(ms) // 2]
+        rate = f / (t * 1e-3) / 1e12
+        tk = ticks.view(n_wg, 4).cpu().double()
+        dt, dr = tk[:, 1] - tk[:, 0], tk[:, 3] - tk[:, 2]
+        ok = dr > 0
+        tick_ghz = float((dt[ok] / dr[ok]).median()) * wall_khz / 1e6 if ok.any() else None
+        out[f"probe_{name}"] = {"tflops": round(rate, 1), "ms": round(t, 4),
+                                "effective_clock_ghz": round(rate * 1e12 / (cu * per_clk) / 1e9,
+                                                             4),
+                                "shader_tick_clock_ghz": None if tick_ghz is None
+                                else round(tick_ghz, 4)}
+    return out
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -366,6 +404,14 @@ def main():
         c.release()
         log(f"[bench] {name}: {ms:.3f} ms/step")
 
+    log("[bench] matrix-core probe (measured-clock peak)")
+    mpeak = measured_peak()
+    log(f"[bench] probe {mpeak}")
+    for e in extra.values():
+        if "frac_of_fp8_peak" in e:
+            e["frac_of_measured_fp8"] = round(e["effective_tflops_attention"]
+                                              / mpeak["probe_fp8"]["tflops"], 4)
+
     recall = None
     if not a.no_recall:
         log("[bench] teacher tile-map recall")
@@ -404,7 +450,10 @@ def main():
                      "traffic_unit": "bytes per launch (HBM, scaled rocprofv3 counters)",
                      "kernel": kname,
                      "per_launch_flop": flops, "avg_launch_ms": round(attn_ms, 4),
-                     "tile_granular_flop": 4.0 * w.d * 64 * 64 * kept},
+                     "tile_granular_flop": 4.0 * w.d * 64 * 64 * kept,
+                     "peak_measured": mpeak["probe_bf16"]["tflops"],
+                     "frac_of_measured": round(achieved / mpeak["probe_bf16"]["tflops"], 4)},
+        "measured_peak": mpeak,
         "cpu_baseline": cpu,
         "effective_tflop_per_layer": flops / 1e12,
         "attention_ms": round(attn_ms, 4),

@@ -23,7 +23,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libvsa.so")
 
 SOURCES = ["plan.cpp", "abi.hip", "map_gather.hip", "pool_score.hip", "select.hip",
-           "attn_bf16.hip", "attn_f32.hip", "teacher.hip", "quant_fp8.hip", "attn_fp8.hip"]
+           "attn_bf16.hip", "attn_f32.hip", "teacher.hip", "quant_fp8.hip", "attn_fp8.hip",
+           "probe.hip"]
 # Per-source extra flags (none needed at present).
 EXTRA: dict = {}
 ARCH = "gfx950"

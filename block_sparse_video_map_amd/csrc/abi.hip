@@ -294,4 +294,29 @@ VSA_API int vsa_sparse_attn_fwd_fp8(const vsa_problem *prob, const void *q8, con
                                          (hipStream_t)stream));
 }
 
+VSA_API int vsa_device_clocks(int32_t *cu_count, int32_t *clock_khz, int32_t *wall_khz) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return VSA_ERR_HIP;
+  const hipDeviceAttribute_t attr[3] = {hipDeviceAttributeMultiprocessorCount,
+                                        hipDeviceAttributeClockRate,
+                                        hipDeviceAttributeWallClockRate};
+  int32_t *dst[3] = {cu_count, clock_khz, wall_khz};
+  for (int i = 0; i < 3; ++i) {
+    if (!dst[i]) continue;
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, attr[i], dev) != hipSuccess) return VSA_ERR_HIP;
+    *dst[i] = v;
+  }
+  return VSA_OK;
+}
+
+VSA_API int vsa_mfma_probe(int32_t kind, int32_t iters, int32_t n_workgroups, uint64_t *ticks,
+                           void *stream) {
+  if (kind != 0 && kind != 1) return VSA_ERR_INVALID_ARG;
+  if (iters < 1 || n_workgroups < 1) return VSA_ERR_INVALID_ARG;
+  if (iters > (1 << 22) || n_workgroups > (1 << 16)) return VSA_ERR_SIZE;
+  if ((uintptr_t)ticks & 7u) return VSA_ERR_INVALID_ARG;
+  return hip_status(launch_mfma_probe(kind, iters, n_workgroups, ticks, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -72,6 +72,11 @@ hipError_t launch_teacher(const Plan &p, const void *qt, const void *kt, const i
 hipError_t launch_quant_fp8(const Plan &p, const void *qt, const void *kt, const void *vt,
                             uint8_t *q8, uint8_t *k8, uint8_t *v8, uint8_t *scales,
                             hipStream_t stream);
+// Matrix-core rate probe (kind 0 bf16, 1 fp8): 256-thread workgroups, each
+// wave `iters` trips of four MFMAs; ticks (or null) gets 4 counters per
+// workgroup.
+hipError_t launch_mfma_probe(int kind, int iters, int n_workgroups, uint64_t *ticks,
+                             hipStream_t stream);
 namespace vsa {
 hipError_t launch_attn_fp8(const Plan &p, const uint8_t *q8, const uint8_t *k8,
                            const uint8_t *v8, const uint8_t *scales, const int32_t *s2t,

@@ -32,7 +32,8 @@ EXPORTS = ("vsa_query_sizes", "vsa_pooled_bytes", "vsa_map_tiles", "vsa_tile_sco
            "vsa_count_flops", "vsa_ref_sizes", "vsa_ref_pooled_bytes", "vsa_ref_scores",
            "vsa_ref_select", "vsa_sparse_attn_fwd_ref", "vsa_kept_stats_ref",
            "vsa_count_flops_ref", "vsa_teacher_map", "vsa_quantize_fp8", "vsa_map_tiles_fp8",
-           "vsa_sparse_attn_fwd_fp8", "vsa_status_string", "vsa_version")
+           "vsa_sparse_attn_fwd_fp8", "vsa_device_clocks", "vsa_mfma_probe",
+           "vsa_status_string", "vsa_version")
 
 
 class vsa_problem(ctypes.Structure):
@@ -104,6 +105,8 @@ def lib() -> ctypes.CDLL:
             "vsa_quantize_fp8": [P, vp, vp, vp, vp, vp, vp, vp, vp],
             "vsa_map_tiles_fp8": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "vsa_sparse_attn_fwd_fp8": [P, vp, vp, vp, vp, vp, vp, f64, R, vp, f32, vp, vp, vp],
+            "vsa_device_clocks": [ctypes.POINTER(i32)] * 3,
+            "vsa_mfma_probe": [i32, i32, i32, vp, vp],
             "vsa_status_string": [ctypes.c_int],
             "vsa_version": [],
         }
@@ -459,6 +462,31 @@ def vsa_sparse_attn_fwd_fp8(prob: Problem, q8, k8, v8, scales, slot_to_token, kv
         prob.ref, _ptr(q8), _ptr(k8), _ptr(v8), _ptr(scales), _ptr(slot_to_token), _ptr(kv_idx),
         float(sparsity), None if budget is None else ctypes.byref(budget), _ptr(ref_idx),
         float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+# ------------------------------------------------------- measurement aids
+
+MFMA_PROBE_FLOPS = (32 * 32 * 16 * 2, 32 * 32 * 64 * 2)   # per MFMA: bf16, fp8
+
+
+def vsa_device_clocks():
+    """(compute units, engine clock in kHz, real-time counter rate in kHz) of
+    the current device, as the runtime reports them."""
+    cu, clk, wall = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check("vsa_device_clocks", lib().vsa_device_clocks(ctypes.byref(cu), ctypes.byref(clk),
+                                                        ctypes.byref(wall)))
+    return cu.value, clk.value, wall.value
+
+
+def vsa_mfma_probe(kind: int, iters: int, n_workgroups: int, ticks=None, stream=None) -> int:
+    """Enqueues the matrix-core load (kind 0 bf16, 1 fp8); ticks is an int64
+    device tensor of 4 * n_workgroups counters or None. Returns the flops
+    the launch performs."""
+    import torch
+    _need(ticks, 4 * n_workgroups, torch.int64, "ticks")
+    _check("vsa_mfma_probe", lib().vsa_mfma_probe(int(kind), int(iters), int(n_workgroups),
+                                                  _ptr(ticks), _stream(stream)))
+    return n_workgroups * 16 * iters * MFMA_PROBE_FLOPS[kind]
 
 
 # ---------------------------------------------------------- whole-layer helper

@@ -398,6 +398,32 @@ VSA_API int vsa_sparse_attn_fwd_fp8(const vsa_problem *prob, const void *q8, con
                                     const int32_t *ref_idx, float softmax_scale, void *out,
                                     float *lse, void *stream);
 
+/*
+ * Measurement aids for the rooflines; neither is a step of the method.
+ *
+ * vsa_device_clocks - the current HIP device's compute-unit count, the
+ * engine clock the runtime reports for it (kHz; its maximum, the clock the
+ * published matrix-core peaks assume) and the rate of its constant
+ * real-time counter (kHz). The dense bf16 peak at a clock f is
+ * CUs x f x 4096 flop per clock (twice that for fp8). Any pointer may be
+ * NULL. VSA_ERR_HIP if the runtime call fails (for instance, no device).
+ *
+ * vsa_mfma_probe - a pure matrix-core load, to measure the rate and clock
+ * the chip sustains under it. n_workgroups workgroups of 256 threads (4
+ * waves); every wave runs `iters` trips of 4 independent MFMAs:
+ *   kind 0: bf16 32x32x16   (32768 flop each, the bf16 attention's type)
+ *   kind 1: E4M3 32x32x64 with unit block scales (131072 flop each)
+ * so one launch performs n_workgroups * 16 * iters MFMAs. ticks: device
+ * uint64 [n_workgroups][4] or NULL; wave 0 of workgroup w writes the shader
+ * tick counter before and after its loop (ticks[w][0], [1]) and the
+ * real-time counter likewise ([2], [3]), 8-byte aligned. Nothing else is
+ * written. 1 <= iters <= 2^22 and 1 <= n_workgroups <= 2^16
+ * (VSA_ERR_SIZE above, VSA_ERR_INVALID_ARG below or for another kind).
+ */
+VSA_API int vsa_device_clocks(int32_t *cu_count, int32_t *clock_khz, int32_t *wall_khz);
+VSA_API int vsa_mfma_probe(int32_t kind, int32_t iters, int32_t n_workgroups, uint64_t *ticks,
+                           void *stream);
+
 /* Static text for a vsa_status value. */
 VSA_API const char *vsa_status_string(int status);
 

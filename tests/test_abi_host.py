@@ -355,3 +355,21 @@ def test_fused_map_fp8_rejects_before_any_launch():
     a = list(args)
     a[7] = ctypes.c_void_p((1 << 20) + 8)       # q8 not 16-byte aligned
     assert L.vsa_map_tiles_fp8(pb.ref, *a, None) == vsa.VSA_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------- measurement aids
+
+def test_mfma_probe_rejects_before_any_launch():
+    L = vsa.lib()
+    assert L.vsa_mfma_probe(2, 1, 1, None, None) == vsa.VSA_ERR_INVALID_ARG
+    assert L.vsa_mfma_probe(0, 0, 1, None, None) == vsa.VSA_ERR_INVALID_ARG
+    assert L.vsa_mfma_probe(1, 1, 0, None, None) == vsa.VSA_ERR_INVALID_ARG
+    assert L.vsa_mfma_probe(0, (1 << 22) + 1, 1, None, None) == vsa.VSA_ERR_SIZE
+    assert L.vsa_mfma_probe(0, 1, (1 << 16) + 1, None, None) == vsa.VSA_ERR_SIZE
+    assert L.vsa_mfma_probe(0, 1, 1, ctypes.c_void_p((1 << 20) + 4),
+                            None) == vsa.VSA_ERR_INVALID_ARG
+
+
+def test_mfma_probe_flop_count():
+    # one 32x32xK product is 2*32*32*K flops; a workgroup has 4 waves of 4 chains
+    assert vsa.MFMA_PROBE_FLOPS == (2 * 32 * 32 * 16, 2 * 32 * 32 * 64)
