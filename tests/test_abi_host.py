@@ -373,3 +373,36 @@ def test_mfma_probe_rejects_before_any_launch():
 def test_mfma_probe_flop_count():
     # one 32x32xK product is 2*32*32*K flops; a workgroup has 4 waves of 4 chains
     assert vsa.MFMA_PROBE_FLOPS == (2 * 32 * 32 * 16, 2 * 32 * 32 * 64)
+
+
+# ------------------------------------------------- random geometries (planner)
+
+from hypothesis import given, settings, strategies as st   # noqa: E402
+
+_SHAPES = [(1 << a, 1 << b, 1 << (6 - a - b)) for a in range(7) for b in range(7 - a)]
+
+
+@settings(max_examples=150, deadline=None)
+@given(T=st.integers(1, 12), Hv=st.integers(1, 20), Wv=st.integers(1, 20),
+       prefix=st.lists(st.integers(0, 300), max_size=4),
+       shapes=st.lists(st.sampled_from(_SHAPES), min_size=1, max_size=4),
+       H=st.integers(1, 6), sparsity=st.floats(0.0, 0.999))
+def test_planner_matches_oracle_on_random_geometries(T, Hv, Wv, prefix, shapes, H, sparsity):
+    """Tile counts, k per shape and the kept pair count of the host planner
+    equal what the oracle's tile map and keep rule give, for any grid, any
+    prefix (empty segments included) and any mix of tile shapes."""
+    p = vsa.Problem(1, H, 64, (T, Hv, Wv), prefix, shapes, "bf16")
+    sz = vsa.vsa_query_sizes(p, sparsity)
+    tms = [oracle.tile_map(T, Hv, Wv, prefix, s) for s in shapes]
+    assert sz.n_prefix_tiles == tms[0].n_prefix_tiles == sum(-(-L // 64) for L in prefix)
+    for i, tm in enumerate(tms):
+        assert (sz.n_tiles[i], sz.n_video_tiles[i]) == (tm.n_tiles, tm.n_video_tiles)
+        assert sz.k[i] == (tm.n_video_tiles if sparsity == 0.0
+                           else oracle.keep_count(sparsity, tm.n_video_tiles))
+    kept, _ = vsa.vsa_kept_stats(p, sparsity)
+    want = 0
+    for h in range(H):
+        tm = tms[h % len(shapes)]
+        k = sz.k[h % len(shapes)]
+        want += tm.n_prefix_tiles * tm.n_tiles + tm.n_video_tiles * (tm.n_prefix_tiles + k)
+    assert kept == want
