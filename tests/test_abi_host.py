@@ -406,3 +406,31 @@ def test_planner_matches_oracle_on_random_geometries(T, Hv, Wv, prefix, shapes, 
         k = sz.k[h % len(shapes)]
         want += tm.n_prefix_tiles * tm.n_tiles + tm.n_video_tiles * (tm.n_prefix_tiles + k)
     assert kept == want
+
+
+@settings(max_examples=60, deadline=None)
+@given(T=st.integers(1, 6), Hv=st.integers(1, 12), Wv=st.integers(1, 12),
+       prefix=st.lists(st.integers(0, 200), max_size=3),
+       shapes=st.lists(st.sampled_from(_SHAPES), min_size=1, max_size=3),
+       H=st.integers(1, 4), sparsity=st.floats(0.05, 0.95), seed=st.integers(0, 2**31 - 1))
+def test_count_flops_matches_oracle_on_random_geometries(T, Hv, Wv, prefix, shapes, H, sparsity,
+                                                         seed):
+    """Effective FLOPs from the host counter equal the oracle's count of real
+    (query, allowed key) pairs for random selections, padded tiles included."""
+    p = vsa.Problem(1, H, 64, (T, Hv, Wv), prefix, shapes, "bf16")
+    sz = vsa.vsa_query_sizes(p, sparsity)
+    tms = [oracle.tile_map(T, Hv, Wv, prefix, s) for s in shapes]
+    s2t = np.full((len(shapes), sz.max_tiles * 64), -1, dtype=np.int32)
+    for i, tm in enumerate(tms):
+        s2t[i, : tm.n_tiles * 64] = tm.slot_to_token
+    rng = np.random.default_rng(seed)
+    kv = np.full((H, sz.max_video_tiles, sz.k_max), -1, dtype=np.int32)
+    want = 0
+    for h in range(H):
+        i = h % len(shapes)
+        tm, k = tms[i], sz.k[i]
+        sel = np.sort(np.stack([rng.choice(tm.n_video_tiles, k, replace=False)
+                                for _ in range(tm.n_video_tiles)]), axis=1)
+        kv[h, : tm.n_video_tiles, :k] = sel
+        want += oracle.effective_flops(tm, oracle.allowed_tiles(tm, sel), 64)
+    assert vsa.vsa_count_flops(p, sparsity, s2t, kv) == want
