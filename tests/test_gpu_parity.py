@@ -132,6 +132,10 @@ def _pick_tiles(tm, count, seed):
 
 
 def test_attention_matches_oracle(run):
+    """Outputs of every sampled query tile against the oracle on the GPU's own
+    selection. The selection itself is checked by the band rule
+    (test_select_topk_bit_exact), so a legitimate near-tie choice never
+    removes a tile from the output comparison."""
     name = run.name
     w, sz = run.w, _sizes(run)
     heads, count = PLAN[name]
@@ -143,13 +147,13 @@ def test_attention_matches_oracle(run):
         tiles = _pick_tiles(tm, count, seed=1000 + h)
         r, _ = _oracle(name, h)
         gpu_sel = kv[h, : tm.n_video_tiles, : r["k"]].cpu().numpy()
-        same_sel = [t for t in tiles if t < tm.n_prefix_tiles
-                    or np.array_equal(gpu_sel[t - tm.n_prefix_tiles],
-                                      r["kv_video"][t - tm.n_prefix_tiles])]
-        assert len(tiles) - len(same_sel) <= max(1, len(tiles) // 100)
-        gs.log(f"[parity] attention {name} head {h}: {len(same_sel)} query tiles")
-        ro, _ = _oracle(name, h, query_tiles=same_sel)
-        rows = np.concatenate([tm.tile_tokens(t) for t in same_sel])
+        differ = sum(1 for t in tiles if t >= tm.n_prefix_tiles
+                     and not np.array_equal(gpu_sel[t - tm.n_prefix_tiles],
+                                            r["kv_video"][t - tm.n_prefix_tiles]))
+        gs.log(f"[parity] attention {name} head {h}: {len(tiles)} query tiles, "
+               f"{differ} with a near-tie selection differing from the oracle's")
+        ro, _ = gs.oracle_head(w, h, query_tiles=tiles, kv_video=gpu_sel)
+        rows = np.concatenate([tm.tile_tokens(t) for t in tiles])
         got = gs.tensor_f32(out[0, h])[rows]
         want = ro["out"][rows]
         got_lse = lse[0, h].cpu().numpy()[rows]
