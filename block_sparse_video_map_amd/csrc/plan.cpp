@@ -67,6 +67,7 @@ int make_plan_geometry(const vsa_problem *prob, Plan *p) {
     p->grid_t[s] = (int32_t)gt; p->grid_h[s] = (int32_t)gh; p->grid_w[s] = (int32_t)gw;
     p->video_full[s] = prob->T % pt == 0 && prob->Hv % ph == 0 && prob->Wv % pw == 0;
     p->n_vt[s] = (int32_t)nvt;
+    if (nvt + p->n_prefix_tiles > VSA_MAX_TILES) return VSA_ERR_SIZE;
     p->n_tiles[s] = (int32_t)(nvt + p->n_prefix_tiles);
     if (p->n_tiles[s] > p->max_tiles) p->max_tiles = p->n_tiles[s];
     if (p->n_vt[s] > p->max_vt) p->max_vt = p->n_vt[s];
@@ -116,6 +117,7 @@ int apply_ref_budget(const vsa_ref_budget *rb, Plan *p) {
   const int t0 = p->prefix_tile0[rb->segment];
   const int n = p->prefix_tile0[rb->segment + 1] - t0;
   if (n < 1) return VSA_ERR_INVALID_ARG;
+  if (n > VSA_MAX_VIDEO_TILES) return VSA_ERR_SIZE;     // the select row length limit
   if (rb->k_ref < 1 || rb->k_ref > n) return VSA_ERR_INVALID_ARG;
   p->ref_t0 = t0;
   p->n_ref = n;

@@ -24,7 +24,7 @@ VSA_F32, VSA_BF16 = 0, 1
 VSA_SCORE_MEAN_GATE, VSA_SCORE_TRIPPOOL = 0, 1
 VSA_SCORE_TRIPPOOL_MAXMIN, VSA_SCORE_TRIPPOOL_AVG = 2, 3
 VSA_TILE, VSA_MAX_SEGMENTS, VSA_MAX_SHAPES = 64, 8, 16
-VSA_MAX_VIDEO_TILES, VSA_MAX_PROJ = 8192, 64
+VSA_MAX_VIDEO_TILES, VSA_MAX_PROJ, VSA_MAX_TILES = 8192, 64, 16383
 
 # Names declared in include/vsa.h.
 EXPORTS = ("vsa_query_sizes", "vsa_pooled_bytes", "vsa_map_tiles", "vsa_tile_scores",

@@ -50,6 +50,9 @@ extern "C" {
 #define VSA_MAX_SEGMENTS 8          /* prefix segments */
 #define VSA_MAX_SHAPES 16           /* distinct per-head tile shapes */
 #define VSA_MAX_VIDEO_TILES 8192    /* video tiles per head (top-k row length) */
+#define VSA_MAX_TILES 16383         /* prefix + video tiles per head: keeps every byte
+                                       offset inside one head's tiled copy below 2^31 and
+                                       every 32-key unit index below 2^15 */
 #define VSA_MAX_PROJ 64             /* TripPool projection width */
 
 typedef enum vsa_status {

@@ -119,6 +119,9 @@ def test_count_flops_matches_oracle_on_host_arrays():
     (dict(grid=(0, 8, 8)), vsa.VSA_ERR_INVALID_ARG),
     (dict(prefix=(-1,)), vsa.VSA_ERR_INVALID_ARG),
     (dict(grid=(1, 1, 64 * 8193), prefix=(), tile_shapes=((1, 1, 64),)), vsa.VSA_ERR_SIZE),
+    # 8192 video tiles plus 8193 prefix tiles: more tiles per head than VSA_MAX_TILES
+    (dict(grid=(1, 1, 64 * 8192), prefix=(64 * 8193,), tile_shapes=((1, 1, 64),)),
+     vsa.VSA_ERR_SIZE),
 ])
 def test_invalid_problems_rejected(change, status):
     w = WORKLOADS["1"]
@@ -253,6 +256,19 @@ def test_bad_ref_budgets_rejected(segment, k_ref):
     with pytest.raises(vsa.VSAError) as e:
         vsa.vsa_ref_sizes(p, vsa.ref_budget(segment, k_ref))
     assert e.value.status == vsa.VSA_ERR_INVALID_ARG
+
+
+def test_long_reference_segment_rejected():
+    """A reference segment longer than a select row (VSA_MAX_VIDEO_TILES tiles)
+    is refused before any launch."""
+    w = WORKLOADS["1"]
+    p = _problem(w, prefix=(40, 64 * (vsa.VSA_MAX_VIDEO_TILES + 1), 24))
+    with pytest.raises(vsa.VSAError) as e:
+        vsa.vsa_ref_sizes(p, vsa.ref_budget(1, 32))
+    assert e.value.status == vsa.VSA_ERR_SIZE
+    p = _problem(w, prefix=(40, 64 * vsa.VSA_MAX_VIDEO_TILES, 24))
+    n, _, _ = vsa.vsa_ref_sizes(p, vsa.ref_budget(1, 32))
+    assert n == vsa.VSA_MAX_VIDEO_TILES
 
 
 def test_zero_length_reference_segment_rejected():
