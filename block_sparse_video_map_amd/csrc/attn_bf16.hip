@@ -1,43 +1,43 @@
 // Step 4 (bf16): tile-skipping flash attention on the 32x32x16 bf16 MFMA.
 //
-// Work unit: one 64-token query tile per workgroup of eight waves, two per
-// SIMD. The tile's key-tile list (all prefix tiles, then its kept video
-// tiles; every tile for a prefix query tile) is dealt round-robin to four
-// key splits; each split is served by two waves, one per 32-query half.
-// Every split keeps its own running max, sum and output; the four are merged
-// in LDS at the end. One query tile per CU keeps the key tiles that
-// neighbouring query tiles share close together in time, so that they hit
-// in the XCD's L2.
+// Work unit: a workgroup of eight waves takes two neighbouring query tiles
+// of one head, A and B (prefix query tiles pair with prefix query tiles and
+// video with video; an odd one out goes alone). A query tile's key list (all
+// prefix tiles, then its kept video tiles; every tile for a prefix query
+// tile) is cut into 32-key units, and units without a real key are dropped.
+// A unit both tiles keep is one shared step; the i-th unit only A keeps and
+// the i-th unit only B keeps form one paired step. Every wave therefore has
+// work in every step, and each K/V byte a shared step copies serves both
+// tiles (neighbouring tiles share most of their kept tiles). Membership
+// comes from a bitmap of each row's tiles, so the order of the indices does
+// not matter. Steps are dealt round-robin to two key splits; a split is four
+// waves (two tiles x two 32-query halves), one per SIMD.
 //
-// The two waves of a split share each K/V tile through LDS: a 32-key half
-// ("unit") of a tile is copied from HBM straight into a two-slot LDS ring of
-// the split by direct-to-LDS buffer loads (wave 0 copies the K blocks, wave
-// 1 the V blocks; no registers held while in flight), one unit ahead of its
-// use. Only the two waves of a split wait for each other, once per unit,
-// through a pair of LDS counters ("next slot landed", "this slot read by
-// both"); the four splits drift freely, so on each SIMD one split's softmax
-// (VALU) tends to overlap another split's products (MFMA). A workgroup-wide
-// barrier per unit instead keeps all eight waves in step and measured 3.7%
-// slower.
+// A split's K and V go through two-slot LDS rings filled by direct-to-LDS
+// buffer loads (each of the four waves copies its share; no registers held
+// while in flight): K two steps ahead of use, V one. The four waves wait for
+// each other once per step through LDS counters; the wait is bounded, and a
+// wave that gives up makes the workgroup write NaN. The step lists are built
+// once per workgroup in LDS, so the loop reads one entry per step.
 //
-// The products are taken transposed, S^T = K Q^T and O^T = V^T P^T, so that
-// every lane owns one query column: the S^T accumulator is already the B
-// operand of the PV product once converted to bf16, and a rescale of O is
-// one scalar per lane. Q/K tiles are stored in the MFMA operand order and V
-// tiles in the matching column order, so every operand block is a
-// contiguous 1 KB wave access.
+// Each wave owns 32 query columns: S^T = K Q^T and O^T = V^T P^T, so the S^T
+// accumulator is already the B operand of the PV product once converted to
+// bf16, and a rescale of O is one scalar per lane. A step issues its sixteen
+// MFMAs in a fixed order (the PV product of the previous step interleaved
+// with the S^T product of the next) with the softmax of the current step
+// spread between them, so one wave keeps the matrix pipe busy while it
+// computes exponentials.
 //
 // The running max is an integer in log2 units, raised only when needed: a
 // unit's probabilities are formed against the current max, and only when
 // some lane's sum over the unit exceeds 2^8 (which any logit more than 8
-// above the max causes) is the true row max taken, O and the sum rescaled and
-// the unit redone. Row sums are taken over the bf16-rounded probabilities
-// that enter the PV product, so numerator and denominator use the same
-// weights.
+// above the max causes) is the true column max taken, O and the sum rescaled
+// and the unit redone. Row sums are taken over the bf16-rounded
+// probabilities that enter the PV product.
 //
 // Workgroups are renumbered so that each of the eight XCDs (which receive
-// workgroup ids round-robin) walks a contiguous run of query tiles of the
-// same head.
+// workgroup ids round-robin) walks a contiguous run of query-tile pairs.
+#include <algorithm>
 #include <cstdlib>
 
 #include "attn_common.h"
@@ -46,262 +46,670 @@
 namespace vsa {
 namespace {
 
-constexpr int kSplits = 4;                   // key splits per query tile
-constexpr int kWaves = 2 * kSplits;          // two query halves per split
+constexpr int kSplits = 2;                       // key splits per workgroup
+constexpr int kWaves = 8;                        // splits x two tiles x two query halves
 constexpr int kThreads = 64 * kWaves;
+constexpr int kRowCap = 1024;                    // key tiles per row of a merged pair list
+constexpr int kStepCap = 4 * kRowCap;            // steps per chunk
+constexpr int kStepStride = kStepCap / kSplits;  // steps per split
+constexpr int kChunkTiles = kStepCap / 2;        // key tiles per chunk of a shared list
+constexpr uint32_t kNone = 0xFFFF;               // no unit for this tile in a step
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -1.0e30f;
 constexpr float kSumLimit = 256.0f;
+constexpr int kGuard = 1 << 20;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Query tiles per workgroup: pairs of neighbouring query tiles of one head.
+struct PairGrid {
+  int32_t n_wg[VSA_MAX_SHAPES];   // workgroups per head of each shape
+  int64_t wg_per_cycle;           // over one cycle of shapes
+  int64_t wg_per_batch;
+  int32_t total;
+  int32_t pair_video;             // video query rows are paired (their lists fit)
+};
 
 __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Four consecutive 1 KiB blocks to LDS; one LDS base (M0) and one global
+// offset, the instruction offset moving both alike.
+__device__ inline void copy4k(__amdgpu_buffer_rsrc_t r, lds_ptr_t dst, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 1024, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 2048, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 3072, 0);
+}
+__device__ inline void copy2k(__amdgpu_buffer_rsrc_t r, lds_ptr_t dst, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 1024, 0);
+}
+
+__device__ inline int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Real keys among the 32 slots of key half kb of `tile` (shape s).
+__device__ inline int unit_real(const Plan &p, int s, int tile, int kb) {
+  if (tile < p.n_prefix_tiles) {
+    int seg = 0;
+    while (seg + 1 < p.n_prefix && tile >= p.prefix_tile0[seg + 1]) ++seg;
+    const int r = p.prefix_len[seg] - (tile - p.prefix_tile0[seg]) * kTile - 32 * kb;
+    return r < 0 ? 0 : (r > 32 ? 32 : r);
+  }
+  if (p.video_full[s]) return 32;
+  const int v = tile - p.n_prefix_tiles;
+  const int gw = p.grid_w[s], gh = p.grid_h[s];
+  const int wi = v % gw, hi = (v / gw) % gh, ti = v / (gw * gh);
+  const int pt = p.shape[s][0], ph = p.shape[s][1], pw = p.shape[s][2];
+  const int rt = min(pt, p.T - ti * pt), rh = min(ph, p.Hv - hi * ph), rw = min(pw, p.Wv - wi * pw);
+  if (rt == pt && rh == ph && rw == pw) return 32;
+  int n = 0;
+  for (int j = 0; j < 32; ++j) {
+    const int slot = kb * 32 + j;
+    const int a = slot / (ph * pw), bb = (slot / pw) % ph, c = slot % pw;
+    n += (a < rt) & (bb < rh) & (c < rw);
+  }
+  return n;
+}
+
+// Query tiles tA, tB (tB < 0: none) of workgroup blockIdx.x, XCD-aware
+// numbering as in work_item.
+__device__ inline void pair_item(const Plan &p, const PairGrid &gd, int &b, int &h, int &tA,
+                                 int &tB) {
+  const int i = blockIdx.x;
+  const int q8 = gd.total / 8;
+  const int L = i < 8 * q8 ? (i % 8) * q8 + i / 8 : i;
+  b = (int)(L / gd.wg_per_batch);
+  const int64_t rem = L % gd.wg_per_batch;
+  const int cyc = (int)(rem / gd.wg_per_cycle);
+  int r = (int)(rem % gd.wg_per_cycle);
+  int s = 0;
+  while (r >= gd.n_wg[s]) {
+    r -= gd.n_wg[s];
+    ++s;
+  }
+  h = cyc * p.n_shapes + s;
+  const int npt = p.n_prefix_tiles;
+  if (p.dense) {
+    tA = 2 * r;
+    tB = tA + 1 < p.n_tiles[s] ? tA + 1 : -1;
+    return;
+  }
+  const int npw = (npt + 1) / 2;
+  if (r < npw) {
+    tA = 2 * r;
+    tB = tA + 1 < npt ? tA + 1 : -1;
+    return;
+  }
+  const int v = r - npw;
+  if (gd.pair_video) {
+    tA = npt + 2 * v;
+    tB = 2 * v + 1 < p.n_vt[s] ? tA + 1 : -1;
+  } else {
+    tA = npt + v;
+    tB = -1;
+  }
+}
+
+// Softmax probabilities of one unit against the running max m (log2 units),
+// rounded to bf16 (the B operand of the PV product), and this lane's sum of
+// the rounded values.
+__device__ __forceinline__ float unit_probs(const f32x16 &sc, float scale_log2, float m,
+                                            bf16x8 &p0, bf16x8 &p1) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) p0[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[e], scale_log2, -m));
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    p1[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[8 + e], scale_log2, -m));
+  float a0 = 0.f, a1 = 0.f;
+  a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p0, p0, 0, 1), ones, a0, false);
+  a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p0, p0, 2, 3), ones, a1, false);
+  a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p0, p0, 4, 5), ones, a0, false);
+  a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p0, p0, 6, 7), ones, a1, false);
+  a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p1, p1, 0, 1), ones, a0, false);
+  a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p1, p1, 2, 3), ones, a1, false);
+  a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p1, p1, 4, 5), ones, a0, false);
+  a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p1, p1, 6, 7), ones, a1, false);
+  return a0 + a1;
+}
+
+// Largest element of a query column over the unit's 32 keys (both lane halves).
+__device__ __forceinline__ float column_max(const f32x16 &sc) {
+  float m = sc[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) m = fmaxf(m, sc[r]);
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m),
+                                                   false, false);
+  return fmaxf(fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])), m);
+}
+
+// Real-key mask (bit = slot within the unit) of unit entry e; 0 for no unit.
+__device__ __forceinline__ uint32_t unit_mask(const Plan &p, int s, uint32_t e, int l32) {
+  if (e == kNone) return 0u;
+  const int tile = (int)((e & 0x7FFF) >> 1), kb = (int)(e & 1);
+  return (uint32_t)__ballot(slot_token(p, s, tile, kb * 32 + l32) >= 0);
+}
+
+// Element r of lane (g, l32) of an S^T block is key (r/4)*8 + g*4 + r%4.
+__device__ __forceinline__ void mask_keys(f32x16 &sc, uint32_t m32, int g) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int k0i = (r / 4) * 8 + g * 4 + (r % 4);
+    sc[r] = ((m32 >> k0i) & 1u) ? sc[r] : -INFINITY;
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_bf16_kernel(Plan p, int total, const bf16_bits *__restrict__ qt,
+void attn_bf16_kernel(Plan p, PairGrid gd, const bf16_bits *__restrict__ qt,
                       const bf16_bits *__restrict__ kt, const bf16_bits *__restrict__ vt,
                       const int32_t *__restrict__ s2t, const int32_t *__restrict__ kv_idx,
                       const int32_t *__restrict__ ref_idx, float scale_log2,
                       bf16_bits *__restrict__ out, float *__restrict__ lse) {
   constexpr int NC = D / 16, NDB = D / 32;
   constexpr int UNIT = 32 * D;                 // elements of one unit's K (or V)
-  // Two slots, each K then V of one unit. Distinct objects: a slot is only
-  // read while the other one is being filled.
-  __shared__ __attribute__((aligned(1024))) bf16_bits ring0_all[kSplits * 2 * UNIT];
-  __shared__ __attribute__((aligned(1024))) bf16_bits ring1_all[kSplits * 2 * UNIT];
-  __shared__ int pair_count[kSplits * 2];      // units finished, per (split, wave)
+  constexpr int UB = UNIT * 2;                 // its bytes
+  constexpr int TB = kTile * D * 2;            // bytes of one tile
+  constexpr int SLOT = 2 * UNIT;               // a split's slot: two units (tile A, tile B)
+  // Issue slots of a step: its 2*NDB + NC MFMAs, at least one per softmax
+  // chunk (sixteen chunks: one element pair every two slots).
+  constexpr int kSlots = 2 * NDB + NC > 16 ? 2 * NDB + NC : 16;
+  // Four distinct slot arrays (K and V, two slots each), so that reads of one
+  // slot never wait for copies landing in another.
+  __shared__ __attribute__((aligned(1024))) bf16_bits kslot0[kSplits * SLOT];
+  __shared__ __attribute__((aligned(1024))) bf16_bits kslot1[kSplits * SLOT];
+  __shared__ __attribute__((aligned(1024))) bf16_bits vslot0[kSplits * SLOT];
+  __shared__ __attribute__((aligned(1024))) bf16_bits vslot1[kSplits * SLOT];
+  __shared__ uint32_t steps[kStepCap];
+  __shared__ uint32_t ulA[2 * kRowCap];
+  __shared__ uint16_t bx[2 * kRowCap];
+  __shared__ __attribute__((aligned(16))) int grp_count[kSplits * 4];
+  __shared__ int scan[2 * kWaves];
+  __shared__ int fault;
 
-  int b, h, tq;
-  work_item(p, total, b, h, tq);
+  int b, h, tA, tB;
+  pair_item(p, gd, b, h, tA, tB);
   const int s = h % p.n_shapes;
   const int bh = b * p.H + h;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
-  const int qb = wave % 2, ks = wave / 2;
-  bf16_bits *const ring0 = ring0_all + ks * 2 * UNIT;
-  bf16_bits *const ring1 = ring1_all + ks * 2 * UNIT;
+  const int sp = wave / 4, role = wave % 4;     // split; role = tile*2 + query half
+  const int tb = role / 2, qb = role % 2;
+  const int myT = tb ? tB : tA;
   const int lane = threadIdx.x % 64;
   const int g = lane / 32, l32 = lane % 32;
   const int npt = p.n_prefix_tiles;
-  const bool full_row = p.dense || tq < npt;
-  const int n_kv = full_row ? p.n_tiles[s] : video_row_len(p, s);
-  // The kept-tile list is read through the constant address space (scalar
-  // loads), which keeps it off the vector-memory counter of the copies.
-  typedef const __attribute__((address_space(4))) int32_t *const_i32_ptr;
-  const const_i32_ptr kv_row =
-      full_row ? nullptr
-               : (const_i32_ptr)(kv_idx + ((int64_t)bh * p.max_vt + (tq - npt)) * p.k_max);
-  const const_i32_ptr ref_row =
-      (full_row || p.n_ref == 0)
-          ? nullptr
-          : (const_i32_ptr)(ref_idx + ((int64_t)bh * p.max_vt + (tq - npt)) * p.k_ref);
+  const bool fullA = p.dense || tA < npt;
+  const bool merge = tB >= 0 && !fullA;         // two video rows with their own lists
   const int64_t head_base = (int64_t)bh * p.max_tiles;
   const int32_t *map = s2t + (int64_t)s * p.max_tiles * kTile;
+  auto kv_row_of = [&](int t) {
+    return kv_idx + ((int64_t)bh * p.max_vt + (t - npt)) * p.k_max;
+  };
+  auto ref_row_of = [&](int t) -> const int32_t * {
+    return p.n_ref == 0 ? nullptr : ref_idx + ((int64_t)bh * p.max_vt + (t - npt)) * p.k_ref;
+  };
 
-  constexpr int TB = kTile * D * 2;
   const uint32_t head_bytes = (uint32_t)p.max_tiles * TB;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(qt + head_base * (kTile * D), head_bytes);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kt + head_base * (kTile * D), head_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vt + head_base * (kTile * D), head_bytes);
   const int voff = lane * 16;
 
-  bf16x8 qf[NC];              // this wave's Q^T fragments (B operand of S^T = K Q^T)
+  if (threadIdx.x < kSplits * 4) grp_count[threadIdx.x] = 0;
+  if (threadIdx.x == 0) fault = 0;
+
+  bf16x8 qf[NC];
+  const int qtile = myT >= 0 ? myT : tA;
 #pragma unroll
-  for (int cc = 0; cc < NC; ++cc) qf[cc] = buffer_load16(rq, voff, tq * TB + (qb * NC + cc) * 1024);
+  for (int cc = 0; cc < NC; ++cc)
+    qf[cc] = buffer_load16(rq, voff, qtile * TB + (qb * NC + cc) * 1024);
+  const bool q_live = myT >= 0 && __any(map[(int64_t)myT * kTile + qb * 32 + l32] >= 0);
   f32x16 o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
   float m_use = kNegBig, l_run = 0.f;
+  bool stalled = false;
+  int sync_n = 0;
 
-  // Global tile of the i-th key tile of the row; ok = false for an index
-  // outside the head's video tiles (then the tile is fully masked).
-  const int n_mine = n_kv > ks ? (n_kv - ks + kSplits - 1) / kSplits : 0;
-  auto tile_of = [&](int i, bool &ok) -> int {
-    ok = true;
-    i = ks + kSplits * i;
-    if (full_row) return i;
-    const int tile = video_row_tile(p, s, i, kv_row, ref_row);
-    if (tile < 0) {
-      ok = false;
-      return 0;
+  // The four waves of a split wait for each other once per step (LDS
+  // counters); bounded, and a wave that gives up poisons the outputs.
+  typedef volatile __attribute__((address_space(3))) int *lds_iptr;
+  typedef volatile __attribute__((address_space(3))) i32x4 *lds_i4ptr;
+  const lds_iptr count = (lds_iptr)grp_count;
+  const lds_i4ptr count4 = (lds_i4ptr)(grp_count + sp * 4);
+  auto grp_sync = [&]() {
+    ++sync_n;
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
+    if (lane == 0) count[sp * 4 + role] = sync_n;
+    if (stalled) return;
+    int guard = 0;
+    for (;;) {
+      const i32x4 c = *count4;
+      if (min(min(c.x, c.y), min(c.z, c.w)) >= sync_n) break;
+      if (++guard > kGuard) {
+        stalled = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
     }
-    return tile;
+    asm volatile("" ::: "memory");
   };
-  // Real-key mask of a tile (bit = slot), ~0 for a full tile.
-  auto tile_mask = [&](int tile, bool ok) -> uint64_t {
-    if (!ok) return 0ull;
-    if (tile_full(p, s, tile)) return ~0ull;
-    return __ballot(slot_token(p, s, tile, lane) >= 0);
+
+  // ---- step lists. A step gives each of the two tiles one 32-key unit
+  // (entry = tile*2 + half, bit 15 for a partly padded half; kNone: none);
+  // both tiles get the same unit when they share it. Step j goes to split
+  // j % 2.
+  auto put_step = [&](int j, uint32_t eA, uint32_t eB) {
+    steps[(j % kSplits) * kStepStride + j / kSplits] = eA | (eB << 16);
   };
-  // Copy of unit (tile, key half kb) into a slot: wave 0 the K blocks, wave 1
-  // the V blocks.
-  auto issue = [&](bf16_bits *slot, int tile, int kb) {
-    if (qb == 0) {
+  // Units of A's entries [e0, e1) as shared steps (both tiles take them).
+  auto build_shared = [&](int e0, int e1) -> int {
+    const int32_t *kv_row = fullA ? nullptr : kv_row_of(tA);
+    const int32_t *ref_row = fullA ? nullptr : ref_row_of(tA);
+    int base = 0;
+    for (int r0 = e0; r0 < e1; r0 += kThreads) {
+      const int e = r0 + (int)threadIdx.x;
+      int tile = -1, n0 = 0, n1 = 0;
+      if (e < e1) {
+        tile = fullA ? e : video_row_tile(p, s, e, kv_row, ref_row);
+        if (tile >= 0) {
+          n0 = unit_real(p, s, tile, 0);
+          n1 = unit_real(p, s, tile, 1);
+        }
+      }
+      const uint64_t b1 = __ballot(n0 > 0 || n1 > 0);
+      const uint64_t b2 = __ballot(n0 > 0 && n1 > 0);
+      const int pre = lanes_below(b1) + lanes_below(b2);
+      if (lane == 0) scan[wave] = __builtin_popcountll(b1) + __builtin_popcountll(b2);
+      __syncthreads();
+      int woff = 0, tot = 0;
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(slot + cc * 512), 16, voff,
-                                                 tile * TB + (kb * NC + cc) * 1024, 0, 0);
-    } else {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rv, (lds_ptr_t)(slot + UNIT + (db * 2 + jj) * 512), 16, voff,
-              tile * TB + (db * 4 + 2 * kb + jj) * 1024, 0, 0);
+      for (int w = 0; w < kWaves; ++w) {
+        const int c = scan[w];
+        woff += w < wave ? c : 0;
+        tot += c;
+      }
+      int pos = base + woff + pre;
+      if (n0 > 0) {
+        const uint32_t u = (uint32_t)(tile * 2) | (n0 < 32 ? 0x8000u : 0u);
+        put_step(pos++, u, u);
+      }
+      if (n1 > 0) {
+        const uint32_t u = (uint32_t)(tile * 2 + 1) | (n1 < 32 ? 0x8000u : 0u);
+        put_step(pos, u, u);
+      }
+      base += tot;
+      __syncthreads();
     }
+    return base;
   };
-  auto frag = [&](const bf16_bits *slot, int blk) -> bf16x8 {
-    return *reinterpret_cast<const bf16x8 *>(slot + blk * 512 + lane * 8);
-  };
-  // P^T of a unit (bf16) against the running max, and the lane's sum of the
-  // rounded probabilities.
-  auto probs = [&](const f32x16 &sc, bf16x8 (&pf)[2]) -> float {
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        pf[j][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[8 * j + e], scale_log2, -m_use));
-      const bf16x8 v = pf[j];
-      a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), ones, a0, false);
-      a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), ones, a1, false);
-      a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), ones, a0, false);
-      a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), ones, a1, false);
+  // Two video rows: units both rows keep are shared steps; the i-th unit only
+  // A keeps and the i-th unit only B keeps make one step. Membership comes
+  // from a bitmap of each row's tiles (LDS, in the K slots before any copy).
+  auto build_merged = [&]() -> int {
+    uint32_t *bmA = reinterpret_cast<uint32_t *>(kslot0);
+    uint32_t *bmB = bmA + (p.max_tiles + 31) / 32;
+    const int words = (p.max_tiles + 31) / 32;
+    for (int i = threadIdx.x; i < 2 * words; i += kThreads) bmA[i] = 0u;
+    __syncthreads();
+    const int n_kv = video_row_len(p, s);
+    const int32_t *kvA = kv_row_of(tA), *kvB = kv_row_of(tB);
+    const int32_t *rfA = ref_row_of(tA), *rfB = ref_row_of(tB);
+    for (int e = threadIdx.x; e < n_kv; e += kThreads) {
+      const int ta = video_row_tile(p, s, e, kvA, rfA), tbb = video_row_tile(p, s, e, kvB, rfB);
+      if (ta >= 0) atomicOr(&bmA[ta >> 5], 1u << (ta & 31));
+      if (tbb >= 0) atomicOr(&bmB[tbb >> 5], 1u << (tbb & 31));
     }
-    return a0 + a1;
+    __syncthreads();
+    int nA = 0, nxA = 0;
+    for (int r0 = 0; r0 < n_kv; r0 += kThreads) {
+      const int e = r0 + (int)threadIdx.x;
+      int tile = -1, n0 = 0, n1 = 0;
+      bool shared = false;
+      if (e < n_kv) {
+        tile = video_row_tile(p, s, e, kvA, rfA);
+        if (tile >= 0) {
+          n0 = unit_real(p, s, tile, 0);
+          n1 = unit_real(p, s, tile, 1);
+          shared = (bmB[tile >> 5] >> (tile & 31)) & 1u;
+        }
+      }
+      const int cnt = (n0 > 0) + (n1 > 0), xc = shared ? 0 : cnt;
+      const uint64_t b1 = __ballot(cnt >= 1), b2 = __ballot(cnt >= 2);
+      const uint64_t x1 = __ballot(xc >= 1), x2 = __ballot(xc >= 2);
+      const int pre = lanes_below(b1) + lanes_below(b2);
+      const int xpre = lanes_below(x1) + lanes_below(x2);
+      if (lane == 0) {
+        scan[wave] = __builtin_popcountll(b1) + __builtin_popcountll(b2);
+        scan[kWaves + wave] = __builtin_popcountll(x1) + __builtin_popcountll(x2);
+      }
+      __syncthreads();
+      int woff = 0, tot = 0, xoff = 0, xtot = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const int c = scan[w], x = scan[kWaves + w];
+        woff += w < wave ? c : 0;
+        tot += c;
+        xoff += w < wave ? x : 0;
+        xtot += x;
+      }
+      int pos = nA + woff + pre, xr = nxA + xoff + xpre;
+      if (n0 > 0) {
+        const uint32_t u = (uint32_t)(tile * 2) | (n0 < 32 ? 0x8000u : 0u);
+        ulA[pos++] = u | (shared ? 0u : (uint32_t)(xr++ + 1) << 16);
+      }
+      if (n1 > 0) {
+        const uint32_t u = (uint32_t)(tile * 2 + 1) | (n1 < 32 ? 0x8000u : 0u);
+        ulA[pos] = u | (shared ? 0u : (uint32_t)(xr + 1) << 16);
+      }
+      nA += tot;
+      nxA += xtot;
+      __syncthreads();
+    }
+    int nxB = 0;
+    for (int r0 = 0; r0 < n_kv; r0 += kThreads) {
+      const int e = r0 + (int)threadIdx.x;
+      int tile = -1, n0 = 0, n1 = 0;
+      if (e < n_kv) {
+        tile = video_row_tile(p, s, e, kvB, rfB);
+        if (tile >= 0 && !((bmA[tile >> 5] >> (tile & 31)) & 1u)) {
+          n0 = unit_real(p, s, tile, 0);
+          n1 = unit_real(p, s, tile, 1);
+        }
+      }
+      const uint64_t b1 = __ballot(n0 > 0 || n1 > 0);
+      const uint64_t b2 = __ballot(n0 > 0 && n1 > 0);
+      const int pre = lanes_below(b1) + lanes_below(b2);
+      if (lane == 0) scan[wave] = __builtin_popcountll(b1) + __builtin_popcountll(b2);
+      __syncthreads();
+      int woff = 0, tot = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const int c = scan[w];
+        woff += w < wave ? c : 0;
+        tot += c;
+      }
+      int pos = nxB + woff + pre;
+      if (n0 > 0) bx[pos++] = (uint16_t)((tile * 2) | (n0 < 32 ? 0x8000 : 0));
+      if (n1 > 0) bx[pos] = (uint16_t)((tile * 2 + 1) | (n1 < 32 ? 0x8000 : 0));
+      nxB += tot;
+      __syncthreads();
+    }
+    const int nS = nA + max(0, nxB - nxA);
+    for (int i = threadIdx.x; i < nS; i += kThreads) {
+      uint32_t eA, eB;
+      if (i < nA) {
+        const uint32_t a = ulA[i];
+        eA = a & 0xFFFFu;
+        const uint32_t x = a >> 16;
+        eB = x == 0 ? eA : (x - 1 < (uint32_t)nxB ? (uint32_t)bx[x - 1] : kNone);
+      } else {
+        eA = kNone;
+        eB = bx[nxA + (i - nA)];
+      }
+      put_step(i, eA, eB);
+    }
+    __syncthreads();
+    return nS;
   };
-  // One unit from a slot: S^T, the mask of a partly filled tile, softmax
-  // (with the rare raise of the max), PV.
-  auto unit = [&](const bf16_bits *slot, uint32_t mask32) {
-    bf16x8 kf[NC];
+
+  const uint32_t *mysteps = steps + sp * kStepStride;
+  auto step_at = [&](int j) -> uint32_t {
+    return __builtin_amdgcn_readfirstlane(mysteps[j]);
+  };
+  auto my_unit = [&](uint32_t st) -> uint32_t { return tb ? (st >> 16) : (st & 0xFFFFu); };
+  auto is_shared = [&](uint32_t st) -> bool { return (st & 0xFFFFu) == (st >> 16); };
+  // This wave's share of the copies of a step. Shared unit: roles 0 and 1
+  // copy the two halves of K, roles 2 and 3 the two halves of V. Separate
+  // units: role 0 copies A's K, role 1 A's V, role 2 B's K, role 3 B's V
+  // (A's unit at offset 0 of the slot, B's at UNIT).
+  auto issue_k = [&](uint32_t st, bf16_bits *slot_all) __attribute__((always_inline)) {
+    bf16_bits *dst = slot_all + sp * SLOT;
+    const uint32_t eA = st & 0xFFFFu, eB = st >> 16;
+    if (eA == eB) {
+      if (role < 2 && eA != kNone) {
+        const int tile = (int)((eA & 0x7FFF) >> 1), kb = (int)(eA & 1);
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) kf[cc] = frag(slot, cc);
-    f32x16 sc;
+        for (int g4 = 0; g4 < NC / 8; ++g4)
+          copy4k(rk, (lds_ptr_t)(dst + (role * (NC / 8) + g4) * 2048), voff,
+                 tile * TB + kb * UB + (role * (NC / 8) + g4) * 4096);
+        if (NC / 8 == 0 && role == 0)            // d = 64: one 4 KiB half
+          copy4k(rk, (lds_ptr_t)dst, voff, tile * TB + kb * UB);
+      }
+    } else if (role == 0 || role == 2) {
+      const uint32_t e = role == 0 ? eA : eB;
+      if (e != kNone) {
+        const int tile = (int)((e & 0x7FFF) >> 1), kb = (int)(e & 1);
+        bf16_bits *d2 = dst + (role / 2) * UNIT;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
-#pragma unroll
-    for (int cc = 0; cc < NC; ++cc) sc = mfma32(kf[cc], qf[cc], sc);
-    __builtin_amdgcn_sched_group_barrier(0x100, NC, 0);   // the NC K fragment reads,
-    __builtin_amdgcn_sched_group_barrier(0x008, NC, 0);   // then the NC S^T products
-    // The V fragments are read now, so their LDS latency hides behind the
-    // softmax instead of stalling each PV product.
-    bf16x8 vf[2 * NDB];
-#pragma unroll
-    for (int j = 0; j < 2 * NDB; ++j) vf[j] = frag(slot + UNIT, j);
-    if (mask32 != 0xFFFFFFFFu) {
-      // Element r of lane (g, l32) is key (r/4)*8 + g*4 + r%4 of the unit.
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int k0i = (r / 4) * 8 + g * 4 + (r % 4);
-        sc[r] = ((mask32 >> k0i) & 1u) ? sc[r] : -INFINITY;
+        for (int g4 = 0; g4 < NC / 4; ++g4)
+          copy4k(rk, (lds_ptr_t)(d2 + g4 * 2048), voff, tile * TB + kb * UB + g4 * 4096);
       }
     }
-    bf16x8 pf[2];
-    float ps = probs(sc, pf);
-    if (__builtin_expect(__any(ps > kSumLimit), 0)) {
-      // A logit exceeded the running max by more than the slack: take the
-      // unit's true row max (both lane halves), move the max there, redo.
-      float m = sc[0];
+  };
+  auto issue_v = [&](uint32_t st, bf16_bits *slot_all) __attribute__((always_inline)) {
+    bf16_bits *dst = slot_all + sp * SLOT;
+    const uint32_t eA = st & 0xFFFFu, eB = st >> 16;
+    if (eA == eB) {
+      if (role >= 2 && eA != kNone) {
+        const int tile = (int)((eA & 0x7FFF) >> 1), kb = (int)(eA & 1);
 #pragma unroll
-      for (int r = 1; r < 16; ++r) m = fmaxf(m, sc[r]);
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m),
-                                                       false, false);
-      m = fmaxf(fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])), m) * scale_log2;
-      const float m_new = fmaxf(ceilf(fmaxf(m_use, m)), kNegBig);
-      const float alpha = __builtin_amdgcn_exp2f(m_use - m_new);
-      l_run *= alpha;
+        for (int dd = 0; dd < NDB / 2; ++dd) {
+          const int db = (role - 2) * (NDB / 2) + dd;
+          copy2k(rv, (lds_ptr_t)(dst + db * 1024), voff, tile * TB + db * 4096 + kb * 2048);
+        }
+      }
+    } else if (role == 1 || role == 3) {
+      const uint32_t e = role == 1 ? eA : eB;
+      if (e != kNone) {
+        const int tile = (int)((e & 0x7FFF) >> 1), kb = (int)(e & 1);
+        bf16_bits *d2 = dst + (role / 2) * UNIT;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      m_use = m_new;
-      ps = probs(sc, pf);
-    }
-    l_run += ps;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      o[db] = mfma32(vf[db * 2], pf[0], o[db]);
-      o[db] = mfma32(vf[db * 2 + 1], pf[1], o[db]);
+        for (int db = 0; db < NDB; ++db)
+          copy2k(rv, (lds_ptr_t)(d2 + db * 1024), voff, tile * TB + db * 4096 + kb * 2048);
+      }
     }
   };
-
-  // Wait for the other wave of this split to finish its n-th unit, after
-  // posting our own: own copies landed and own reads of the old slot done
-  // (all counters drained) before the post. The wait is bounded, so it ends
-  // even if the partner never posts (which the schedule below rules out).
-  typedef volatile __attribute__((address_space(3))) int *lds_iptr;
-  const lds_iptr count = (lds_iptr)pair_count;
-  auto pair_sync = [&](int n) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    if (lane == 0) count[ks * 2 + qb] = n;
-    for (int guard = 0; count[ks * 2 + 1 - qb] < n && guard < (1 << 24); ++guard)
-      __builtin_amdgcn_s_sleep(1);
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  auto frag = [&](const bf16_bits *slot_all, int off, int blk) __attribute__((always_inline))
+      -> bf16x8 {
+    return *reinterpret_cast<const bf16x8 *>(slot_all + sp * SLOT + off + blk * 512 + lane * 8);
   };
+  // Offset of this wave's unit in a step's slot.
+  auto unit_off = [&](uint32_t st) -> int { return is_shared(st) ? 0 : tb * UNIT; };
 
-  // Unit 2i + kb is key half kb of the split's i-th tile; even units use slot
-  // ring0, odd units ring1. The copy of the next unit is issued before the
-  // current one is computed. Both waves of a split run the same n_mine steps.
-  bool ok = false;
-  int t = 0;
-  uint64_t mask = 0;
-  if (threadIdx.x < kSplits * 2) pair_count[threadIdx.x] = 0;
-  if (n_mine > 0) {
-    t = tile_of(0, ok);
-    mask = tile_mask(t, ok);
-    issue(ring0, t, 0);
+  const int n_rows = merge ? 1 : (fullA ? p.n_tiles[s] : video_row_len(p, s));
+  const int chunk = merge ? n_rows : kChunkTiles;
+  for (int e0 = 0; e0 < n_rows; e0 += chunk) {
+    const int nS = merge ? build_merged() : build_shared(e0, min(n_rows, e0 + chunk));
+    const int n_u = nS > sp ? (nS - sp + kSplits - 1) / kSplits : 0;
+    if (n_u > 0) {
+      // Step u: K in slot u%2 of the K slots, V in slot u%2 of the V slots.
+      // Step u issues K of step u+2 and V of step u+1, reads K of step u+1
+      // and V of step u, takes the PV product of step u-1, S of step u+1
+      // with the softmax of step u, and ends with the group wait.
+      uint32_t st0 = step_at(0);
+      uint32_t st1 = n_u > 1 ? step_at(1) : kNone | (kNone << 16);
+      uint32_t st2 = n_u > 2 ? step_at(2) : kNone | (kNone << 16);
+      issue_k(st0, kslot0);
+      if (n_u > 1) issue_k(st1, kslot1);
+      issue_v(st0, vslot0);
+      grp_sync();
+      bf16x8 p0, p1;
+      f32x16 sc;
+      const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
+      bf16x8 vf[2 * NDB];
+      if (q_live) {
+        f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        const int off = unit_off(st0);
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) acc = mfma32(frag(kslot0, off, cc), qf[cc], acc);
+        sc = acc;
+        const uint32_t me = my_unit(st0);
+        if (me & 0x8000) mask_keys(sc, unit_mask(p, s, me, l32), g);
+        if (m_use == kNegBig) m_use = fmaxf(ceilf(column_max(sc) * scale_log2), kNegBig);
+#pragma unroll
+        for (int j = 0; j < 2 * NDB; ++j)
+#pragma unroll
+          for (int e8 = 0; e8 < 8; ++e8) vf[j][e8] = (__bf16)0.f;
+#pragma unroll
+        for (int e8 = 0; e8 < 8; ++e8) p0[e8] = p1[e8] = (__bf16)0.f;
+      }
+      grp_sync();
+// One step with a next step: KR/VR the slots read (K of step u+1, V of step
+// u), KW/VW the slots refilled (K of step u+2, V of step u+1). st0/st1/st2:
+// the entries of steps u, u+1, u+2.
+#define VSA_STEP(KR, VR, KW, VW)                                                          \
+  {                                                                                       \
+    if (u + 2 < n_u) issue_k(st2, KW);                                                    \
+    issue_v(st1, VW);                                                                     \
+    const uint32_t pend = mysteps[min(u + 3, n_u - 1)];                                   \
+    if (q_live) {                                                                         \
+      const int koff = unit_off(st1), voff2 = unit_off(st0);                              \
+      bf16x8 kf[NC];                                                                      \
+      _Pragma("unroll") for (int cc = 0; cc < NC; ++cc) kf[cc] = frag(KR, koff, cc);      \
+      f32x16 sn;                                                                          \
+      _Pragma("unroll") for (int r = 0; r < 16; ++r) sn[r] = 0.f;                         \
+      float tt[16];                                                                       \
+      bf16x2 pk[8];                                                                       \
+      float a0 = 0.f, a1 = 0.f;                                                           \
+      __builtin_amdgcn_sched_barrier(0);                                                  \
+      _Pragma("unroll") for (int i = 0; i < kSlots; ++i) {                                \
+        const int n_pv = 2 * NDB;                                                         \
+        const bool is_s = (i < 2) ? false : (i >= n_pv + NC - 2) ? true : (i % 2 == 0);  \
+        const int idx = (i < 2) ? i : (i >= n_pv + NC - 2) ? (i - n_pv)                   \
+                        : (i % 2 == 0) ? (i / 2 - 1) : ((i + 1) / 2);                     \
+        if (i >= n_pv + NC) {                                                             \
+        } else if (!is_s) {                                                               \
+          o[idx / 2] = mfma32(vf[idx], (idx % 2) ? p1 : p0, o[idx / 2]);                  \
+          vf[idx] = frag(VR, voff2, idx);                                                 \
+        } else {                                                                          \
+          sn = mfma32(kf[idx], qf[idx], sn);                                              \
+        }                                                                                 \
+        if (i < 16) {                                                                     \
+          const int k = i / 2;                                                            \
+          if (i % 2 == 0) {                                                               \
+            tt[2 * k] = fmaf(sc[2 * k], scale_log2, -m_use);                              \
+            tt[2 * k + 1] = fmaf(sc[2 * k + 1], scale_log2, -m_use);                      \
+            tt[2 * k] = __builtin_amdgcn_exp2f(tt[2 * k]);                                \
+          } else {                                                                        \
+            tt[2 * k + 1] = __builtin_amdgcn_exp2f(tt[2 * k + 1]);                        \
+            pk[k] = bf16x2{(__bf16)tt[2 * k], (__bf16)tt[2 * k + 1]};                     \
+            if (k % 2 == 0)                                                               \
+              a0 = __builtin_amdgcn_fdot2_f32_bf16(pk[k], ones2, a0, false);              \
+            else                                                                          \
+              a1 = __builtin_amdgcn_fdot2_f32_bf16(pk[k], ones2, a1, false);              \
+          }                                                                               \
+        }                                                                                 \
+        __builtin_amdgcn_sched_barrier(0);                                                \
+      }                                                                                   \
+      p0 = __builtin_shufflevector(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),     \
+                                   __builtin_shufflevector(pk[2], pk[3], 0, 1, 2, 3),     \
+                                   0, 1, 2, 3, 4, 5, 6, 7);                               \
+      p1 = __builtin_shufflevector(__builtin_shufflevector(pk[4], pk[5], 0, 1, 2, 3),     \
+                                   __builtin_shufflevector(pk[6], pk[7], 0, 1, 2, 3),     \
+                                   0, 1, 2, 3, 4, 5, 6, 7);                               \
+      float ps = a0 + a1;                                                                 \
+      if (__builtin_expect(__any(ps > kSumLimit), 0)) {                                   \
+        const float m_new =                                                               \
+            fmaxf(ceilf(fmaxf(m_use, column_max(sc) * scale_log2)), kNegBig);             \
+        const float alpha = __builtin_amdgcn_exp2f(m_use - m_new);                        \
+        l_run *= alpha;                                                                   \
+        _Pragma("unroll") for (int db = 0; db < NDB; ++db)                                \
+          _Pragma("unroll") for (int r = 0; r < 16; ++r) o[db][r] *= alpha;               \
+        m_use = m_new;                                                                    \
+        ps = unit_probs(sc, scale_log2, m_use, p0, p1);                                   \
+      }                                                                                   \
+      l_run += ps;                                                                        \
+      sc = sn;                                                                            \
+      const uint32_t me = my_unit(st1);                                                   \
+      if (me & 0x8000) mask_keys(sc, unit_mask(p, s, me, l32), g);                        \
+    }                                                                                     \
+    grp_sync();                                                                           \
+    st0 = st1;                                                                            \
+    st1 = st2;                                                                            \
+    st2 = __builtin_amdgcn_readfirstlane(pend);                                           \
   }
-  sync_slots();
-  for (int i = 0; i < n_mine; ++i) {
-    issue(ring1, t, 1);
-    unit(ring0, (uint32_t)mask);
-    pair_sync(2 * i + 1);
-    const bool more = i + 1 < n_mine;
-    bool ok1 = false;
-    int t1 = 0;
-    if (more) {
-      t1 = tile_of(i + 1, ok1);
-      issue(ring0, t1, 0);
+      int u = 0;
+      for (; u + 2 < n_u; u += 2) {
+        VSA_STEP(kslot1, vslot0, kslot0, vslot1)
+        ++u;
+        VSA_STEP(kslot0, vslot1, kslot1, vslot0)
+        --u;
+      }
+      if (u + 1 < n_u) {
+        VSA_STEP(kslot1, vslot0, kslot0, vslot1)
+        ++u;
+      }
+#undef VSA_STEP
+      // Last step (V in slot u%2), after the PV product of step u-1.
+      if (q_live) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          o[db] = mfma32(vf[db * 2], p0, o[db]);
+          o[db] = mfma32(vf[db * 2 + 1], p1, o[db]);
+        }
+        float ps = unit_probs(sc, scale_log2, m_use, p0, p1);
+        if (__builtin_expect(__any(ps > kSumLimit), 0)) {
+          const float m_new = fmaxf(ceilf(fmaxf(m_use, column_max(sc) * scale_log2)), kNegBig);
+          const float alpha = __builtin_amdgcn_exp2f(m_use - m_new);
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+          m_use = m_new;
+          ps = unit_probs(sc, scale_log2, m_use, p0, p1);
+        }
+        l_run += ps;
+        const int voff2 = unit_off(st0);
+        const bf16_bits *vl = (u % 2 == 0) ? vslot0 : vslot1;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          o[db] = mfma32(frag(vl, voff2, db * 2), p0, o[db]);
+          o[db] = mfma32(frag(vl, voff2, db * 2 + 1), p1, o[db]);
+        }
+      }
     }
-    unit(ring1, (uint32_t)(mask >> 32));
-    pair_sync(2 * i + 2);
-    t = t1;
-    mask = more ? tile_mask(t1, ok1) : 0ull;
+    __syncthreads();                           // lists and slots free for the next chunk
   }
-  __syncthreads();                             // every split done with its rings
+  if (stalled) fault = 1;
 
-  // Merge the four key splits of each query half (the rings are free now).
-  float *osum = reinterpret_cast<float *>(ring0_all);       // [64][D], swizzled
-  float *sm_m = reinterpret_cast<float *>(ring1_all);       // [kSplits][64]
-  float *sm_l = sm_m + kSplits * kTile;
+  // Merge the two key splits of each (tile, query half); the slots are free.
+  float *osum = reinterpret_cast<float *>(tb ? kslot1 : kslot0);   // [64][D], swizzled
+  float *sm_m = reinterpret_cast<float *>(vslot0);                 // [split][tile][64]
+  float *sm_l = sm_m + kSplits * 2 * kTile;
   const int q = qb * 32 + l32;
   {
     const float lt = l_run + __shfl_xor(l_run, 32);
     if (g == 0) {
-      sm_m[ks * kTile + q] = m_use;
-      sm_l[ks * kTile + q] = lt;
+      sm_m[(sp * 2 + tb) * kTile + q] = m_use;
+      sm_l[(sp * 2 + tb) * kTile + q] = lt;
     }
   }
   __syncthreads();
-  float M = sm_m[q];
+  float M = kNegBig;
 #pragma unroll
-  for (int w = 1; w < kSplits; ++w) M = fmaxf(M, sm_m[w * kTile + q]);
+  for (int w = 0; w < kSplits; ++w) M = fmaxf(M, sm_m[(w * 2 + tb) * kTile + q]);
   float L = 0.f;
 #pragma unroll
-  for (int w = 0; w < kSplits; ++w) L += sm_l[w * kTile + q] * __builtin_amdgcn_exp2f(sm_m[w * kTile + q] - M);
+  for (int w = 0; w < kSplits; ++w)
+    L += sm_l[(w * 2 + tb) * kTile + q] * __builtin_amdgcn_exp2f(sm_m[(w * 2 + tb) * kTile + q] - M);
   const float f = __builtin_amdgcn_exp2f(m_use - M) / L;
   // Element (q, c) of the merged tile sits at q*D + (c ^ (q % 32)).
   for (int turn = 0; turn < kSplits; ++turn) {
-    if (ks == turn) {
+    if (sp == turn) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -316,28 +724,58 @@ void attn_bf16_kernel(Plan p, int total, const bf16_bits *__restrict__ qt,
     }
     __syncthreads();
   }
-  const int32_t *qmap = map + (int64_t)tq * kTile;
+  const bool bad = fault != 0;
   bf16_bits *out_bh = out + (int64_t)bh * p.N * D;
-  for (int idx = threadIdx.x; idx < kTile * D / 8; idx += blockDim.x) {
-    const int row = idx / (D / 8), ch = idx % (D / 8);
-    const int32_t tok = qmap[row];
-    if (tok < 0) continue;
-    bf16x8 v8;
+  for (int t2 = 0; t2 < 2; ++t2) {
+    const int tq = t2 ? tB : tA;
+    if (tq < 0) continue;
+    const int32_t *qmap = map + (int64_t)tq * kTile;
+    const float *os = reinterpret_cast<const float *>(t2 ? kslot1 : kslot0);
+    for (int idx = threadIdx.x; idx < kTile * D / 8; idx += blockDim.x) {
+      const int row = idx / (D / 8), ch = idx % (D / 8);
+      const int32_t tok = qmap[row];
+      if (tok < 0) continue;
+      bf16x8 v8;
 #pragma unroll
-    for (int e8 = 0; e8 < 8; ++e8) v8[e8] = (__bf16)osum[row * D + ((ch * 8 + e8) ^ (row % 32))];
-    *reinterpret_cast<bf16x8 *>(out_bh + (int64_t)tok * D + ch * 8) = v8;
-  }
-  if (lse && threadIdx.x < kTile) {
-    const int qq = threadIdx.x;
-    const int32_t tok = qmap[qq];
-    if (tok >= 0) {
-      float MM = sm_m[qq];
-      for (int w = 1; w < kSplits; ++w) MM = fmaxf(MM, sm_m[w * kTile + qq]);
-      float LL = 0.f;
-      for (int w = 0; w < kSplits; ++w) LL += sm_l[w * kTile + qq] * __builtin_amdgcn_exp2f(sm_m[w * kTile + qq] - MM);
-      lse[(int64_t)bh * p.N + tok] = MM * kLn2 + logf(LL);
+      for (int e8 = 0; e8 < 8; ++e8)
+        v8[e8] = bad ? (__bf16)NAN : (__bf16)os[row * D + ((ch * 8 + e8) ^ (row % 32))];
+      *reinterpret_cast<bf16x8 *>(out_bh + (int64_t)tok * D + ch * 8) = v8;
+    }
+    if (lse && threadIdx.x < kTile) {
+      const int qq = threadIdx.x;
+      const int32_t tok = qmap[qq];
+      if (tok >= 0) {
+        float MM = kNegBig;
+        for (int w = 0; w < kSplits; ++w) MM = fmaxf(MM, sm_m[(w * 2 + t2) * kTile + qq]);
+        float LL = 0.f;
+        for (int w = 0; w < kSplits; ++w)
+          LL += sm_l[(w * 2 + t2) * kTile + qq] *
+                __builtin_amdgcn_exp2f(sm_m[(w * 2 + t2) * kTile + qq] - MM);
+        lse[(int64_t)bh * p.N + tok] = bad ? NAN : MM * kLn2 + logf(LL);
+      }
     }
   }
+}
+
+PairGrid make_grid(const Plan &p) {
+  PairGrid g{};
+  int longest = 0;
+  for (int s = 0; s < p.n_shapes; ++s)
+    longest = std::max(longest, p.n_prefix_tiles - p.n_ref + p.k_ref + p.k[s]);
+  g.pair_video = !p.dense && longest <= kRowCap;
+  for (int s = 0; s < p.n_shapes; ++s) {
+    if (p.dense) {
+      g.n_wg[s] = (p.n_tiles[s] + 1) / 2;
+    } else {
+      g.n_wg[s] = (p.n_prefix_tiles + 1) / 2 + (g.pair_video ? (p.n_vt[s] + 1) / 2 : p.n_vt[s]);
+    }
+  }
+  g.wg_per_cycle = 0;
+  for (int s = 0; s < p.n_shapes; ++s) g.wg_per_cycle += g.n_wg[s];
+  g.wg_per_batch = 0;
+  for (int h = 0; h < p.H; ++h) g.wg_per_batch += g.n_wg[h % p.n_shapes];
+  g.total = (int32_t)(g.wg_per_batch * p.B);
+  return g;
 }
 
 }  // namespace
@@ -345,16 +783,16 @@ void attn_bf16_kernel(Plan p, int total, const bf16_bits *__restrict__ qt,
 hipError_t launch_attn_bf16(const Plan &p, const void *qt, const void *kt, const void *vt,
                             const int32_t *s2t, const int32_t *kv_idx, const int32_t *ref_idx,
                             float scale, void *out, float *lse, hipStream_t stream) {
-  const int total = (int)(p.tiles_per_batch * p.B);
+  const PairGrid gd = make_grid(p);
   const float sl2 = scale * kLog2e;
   if (p.d == 128)
-    hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(total), dim3(kThreads), 0, stream, p,
-                       total, (const bf16_bits *)qt, (const bf16_bits *)kt,
-                       (const bf16_bits *)vt, s2t, kv_idx, ref_idx, sl2, (bf16_bits *)out, lse);
+    hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(gd.total), dim3(kThreads), 0, stream, p, gd,
+                       (const bf16_bits *)qt, (const bf16_bits *)kt, (const bf16_bits *)vt, s2t,
+                       kv_idx, ref_idx, sl2, (bf16_bits *)out, lse);
   else
-    hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(total), dim3(kThreads), 0, stream, p,
-                       total, (const bf16_bits *)qt, (const bf16_bits *)kt,
-                       (const bf16_bits *)vt, s2t, kv_idx, ref_idx, sl2, (bf16_bits *)out, lse);
+    hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(gd.total), dim3(kThreads), 0, stream, p, gd,
+                       (const bf16_bits *)qt, (const bf16_bits *)kt, (const bf16_bits *)vt, s2t,
+                       kv_idx, ref_idx, sl2, (bf16_bits *)out, lse);
   return hipGetLastError();
 }
 
