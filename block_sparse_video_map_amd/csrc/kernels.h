@@ -14,19 +14,23 @@ hipError_t launch_gather(const Plan &p, const void *q, const void *k, const void
                          uint8_t *k8, uint8_t *v8, uint8_t *scales, hipStream_t stream);
 // Tiles to pool: per (batch*head), tiles tile0 .. tile0+ntiles-1 of the tiled
 // copies (ntiles < 0: the head's video tiles); source z of the launch reads
-// src[z] with weights w[z] and writes rows ((z*B*H + bh)*rows + i) of the
-// output.
+// src[z] with weights w[z] and writes rows ((z*nbh + bh - bh0)*rows + i) of
+// the output. The launch covers (batch*head) bh0 .. bh0+nbh-1 (nbh < 0: all).
 struct PoolJob {
   int32_t tile0;
   int32_t ntiles;
   int32_t rows;
   const void *src[2];
   const float *w[2];
+  int32_t bh0 = 0;
+  int32_t nbh = -1;
 };
 
 // Descriptor dot products: rows = the head's video query tiles of q, columns
 // = ncols key descriptors of k (ncols < 0: the head's video tiles), output
-// out[bh*out_bh + i*out_row + j]. q_bh / k_bh: doubles per (batch*head).
+// out[bh*out_bh + i*out_row + j]. q_bh / k_bh: doubles per (batch*head), q and
+// k pointing at (batch*head) bh0; the launch covers bh0 .. bh0+nbh-1 (nbh < 0:
+// all).
 struct ScoreJob {
   const double *q;
   int64_t q_bh;
@@ -36,6 +40,8 @@ struct ScoreJob {
   float *out;
   int64_t out_row;
   int64_t out_bh;
+  int32_t bh0 = 0;
+  int32_t nbh = -1;
 };
 
 // Top-k per row: row i of (batch*head) bh is scores[bh*in_bh + i*in_row],

@@ -72,7 +72,8 @@ __global__ __launch_bounds__(256) void pool_mean_gate_kernel(
   __shared__ double mean[kPoolTiles * LM];   // [tile][channel]
   __shared__ int count[kPoolTiles];
 
-  const int bh = blockIdx.y, which = blockIdx.z;
+  const int bh = job.bh0 + blockIdx.y, which = blockIdx.z;
+  const int nbh = job.nbh < 0 ? p.B * p.H : job.nbh;
   const int h = bh % p.H, s = h % p.n_shapes;
   const int n = job.ntiles < 0 ? p.n_vt[s] : job.ntiles;
   const int vt0 = blockIdx.x * kPoolTiles;
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(256) void pool_mean_gate_kernel(
   // Gate product on the f64 MFMA. A: lane l holds mean[l%16][k0 + l/16];
   // B: gate[k0 + l/16][col0 + l%16]; D element e: row 4e + l/16, column l%16.
   const int l16 = lane % 16, g4 = lane / 16;
-  double *dst = pooled + (((int64_t)which * p.B * p.H + bh) * job.rows + vt0) * D;
+  double *dst = pooled + (((int64_t)which * nbh + bh - job.bh0) * job.rows + vt0) * D;
   for (int cb = wave; cb < D / 16; cb += 4) {
     f64x4 acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll 8
@@ -168,7 +169,8 @@ __global__ __launch_bounds__(256) void pool_trippool_kernel(
   __shared__ double red[3][4][RB * 16];      // [stat][wave][column]
   __shared__ int valid[kTile];
 
-  const int bh = blockIdx.y, which = blockIdx.z;
+  const int bh = job.bh0 + blockIdx.y, which = blockIdx.z;
+  const int nbh = job.nbh < 0 ? p.B * p.H : job.nbh;
   const int h = bh % p.H, s = h % p.n_shapes;
   const int n_rows = job.ntiles < 0 ? p.n_vt[s] : job.ntiles;
   const int first = blockIdx.x * kTripTiles;
@@ -254,7 +256,7 @@ __global__ __launch_bounds__(256) void pool_trippool_kernel(
         tn = fmin(tn, red[2][ww][j]);
       }
       const int width = __builtin_popcount(stats) * R;
-      double *out = pooled + (((int64_t)which * p.B * p.H + bh) * job.rows + vt_i) * width + j;
+      double *out = pooled + (((int64_t)which * nbh + bh - job.bh0) * job.rows + vt_i) * width + j;
       if (stats & 1) {
         *out = ts / (double)n;
         out += R;
@@ -286,7 +288,7 @@ constexpr int kLK = kKC + 2;   // padded LDS row (doubles)
 __global__ __launch_bounds__(256) void scores_kernel(Plan p, int r, ScoreJob job) {
   __shared__ double As[2][kSB * kLK];
   __shared__ double Bs[2][kSB * kLK];
-  const int bh = blockIdx.z, h = bh % p.H, s = h % p.n_shapes;
+  const int bh = job.bh0 + blockIdx.z, h = bh % p.H, s = h % p.n_shapes;
   const int n = p.n_vt[s];                                   // query rows
   const int m = job.ncols < 0 ? n : job.ncols;               // key columns
   const int i0 = blockIdx.y * kSB, j0 = blockIdx.x * kSB;
@@ -295,8 +297,8 @@ __global__ __launch_bounds__(256) void scores_kernel(Plan p, int r, ScoreJob job
   const int wave = __builtin_amdgcn_readfirstlane(t / 64);
   const int lane = t % 64, g = lane / 16, l16 = lane % 16;
   const int wr = (wave / 2) * 32, wc = (wave % 2) * 32;    // wave's block inside the 64x64
-  const double *Qd = job.q + (int64_t)bh * job.q_bh;
-  const double *Kd = job.k + (int64_t)bh * job.k_bh;
+  const double *Qd = job.q + (int64_t)(bh - job.bh0) * job.q_bh;
+  const double *Kd = job.k + (int64_t)(bh - job.bh0) * job.k_bh;
 
   // Thread t stages row t/4, columns 4*(t%4) .. +3 of the chunk, for A and B.
   const int srow = t / 4, scol = (t % 4) * 4;
@@ -368,9 +370,10 @@ template <typename T, int D>
 hipError_t pool_t(const Plan &p, int mode, int R, const PoolJob &job, int nsrc,
                   const int32_t *s2t, double *pooled, hipStream_t st) {
   const int rows = job.ntiles < 0 ? p.max_vt : job.ntiles;
-  dim3 grid((rows + kTripTiles - 1) / kTripTiles, p.B * p.H, nsrc);
+  const int nbh = job.nbh < 0 ? p.B * p.H : job.nbh;
+  dim3 grid((rows + kTripTiles - 1) / kTripTiles, nbh, nsrc);
   if (mode == VSA_SCORE_MEAN_GATE) {
-    dim3 grid_mg((rows + kPoolTiles - 1) / kPoolTiles, p.B * p.H, nsrc);
+    dim3 grid_mg((rows + kPoolTiles - 1) / kPoolTiles, nbh, nsrc);
     hipLaunchKernelGGL((pool_mean_gate_kernel<T, D>), grid_mg, dim3(256), 0, st, p, job, s2t,
                        pooled);
   } else {
@@ -405,7 +408,8 @@ hipError_t launch_pool(const Plan &p, int mode, int proj_dim, const PoolJob &job
 
 hipError_t launch_scores(const Plan &p, int r, const ScoreJob &job, hipStream_t stream) {
   const int cols = job.ncols < 0 ? p.max_vt : job.ncols;
-  dim3 grid((cols + vsa::kSB - 1) / vsa::kSB, (p.max_vt + vsa::kSB - 1) / vsa::kSB, p.B * p.H);
+  const int nbh = job.nbh < 0 ? p.B * p.H : job.nbh;
+  dim3 grid((cols + vsa::kSB - 1) / vsa::kSB, (p.max_vt + vsa::kSB - 1) / vsa::kSB, nbh);
   hipLaunchKernelGGL(vsa::scores_kernel, grid, dim3(256), 0, stream, p, r, job);
   return hipGetLastError();
 }

@@ -25,9 +25,11 @@ VSA_SCORE_MEAN_GATE, VSA_SCORE_TRIPPOOL = 0, 1
 VSA_SCORE_TRIPPOOL_MAXMIN, VSA_SCORE_TRIPPOOL_AVG = 2, 3
 VSA_TILE, VSA_MAX_SEGMENTS, VSA_MAX_SHAPES = 64, 8, 16
 VSA_MAX_VIDEO_TILES, VSA_MAX_PROJ, VSA_MAX_TILES = 8192, 64, 16383
+VSA_NOALLOC_SCRATCH_BYTES = 32 << 20     # fixed device array of vsa_tile_scores_noalloc
 
 # Names declared in include/vsa.h.
 EXPORTS = ("vsa_query_sizes", "vsa_pooled_bytes", "vsa_map_tiles", "vsa_tile_scores",
+           "vsa_tile_scores_noalloc",
            "vsa_select_topk", "vsa_sparse_attn_fwd", "vsa_kept_stats",
            "vsa_count_flops", "vsa_ref_sizes", "vsa_ref_pooled_bytes", "vsa_ref_scores",
            "vsa_ref_select", "vsa_sparse_attn_fwd_ref", "vsa_kept_stats_ref",
@@ -89,6 +91,7 @@ def lib() -> ctypes.CDLL:
             "vsa_pooled_bytes": [P, i32, i32, ctypes.POINTER(i64)],
             "vsa_map_tiles": [P, vp, vp, vp, vp, vp, vp, vp, vp],
             "vsa_tile_scores": [P, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp],
+            "vsa_tile_scores_noalloc": [P, i32, i32, vp, vp, vp, vp, vp, vp, vp],
             "vsa_select_topk": [P, vp, f64, vp, vp],
             "vsa_sparse_attn_fwd": [P, vp, vp, vp, vp, vp, f64, f32, vp, vp, vp],
             "vsa_kept_stats": [P, f64, ctypes.POINTER(i64), ctypes.POINTER(f64)],
@@ -270,6 +273,19 @@ def vsa_tile_scores(prob: Problem, mode: int, proj_dim: int, qt, kt, slot_to_tok
     _check("vsa_tile_scores", lib().vsa_tile_scores(
         prob.ref, int(mode), int(proj_dim), _ptr(qt), _ptr(kt), _ptr(slot_to_token), _ptr(wq),
         _ptr(wk), _ptr(pooled_ws), _ptr(scores), _stream(stream)))
+
+
+def vsa_tile_scores_noalloc(prob: Problem, mode: int, proj_dim: int, qt, kt, slot_to_token, wq,
+                            wk, scores, stream=None):
+    """vsa_tile_scores without a workspace (the library's fixed device array)."""
+    import torch
+    sz = vsa_query_sizes(prob, 0.0)
+    _need(scores, sz.score_elems, torch.float32, "scores")
+    _need(wq, 1, torch.float32, "wq")
+    _need(wk, 1, torch.float32, "wk")
+    _check("vsa_tile_scores_noalloc", lib().vsa_tile_scores_noalloc(
+        prob.ref, int(mode), int(proj_dim), _ptr(qt), _ptr(kt), _ptr(slot_to_token), _ptr(wq),
+        _ptr(wk), _ptr(scores), _stream(stream)))
 
 
 def vsa_select_topk(prob: Problem, scores, sparsity: float, kv_idx, stream=None):

@@ -196,6 +196,27 @@ VSA_API int vsa_tile_scores(const vsa_problem *prob, int32_t mode,
                             void *stream);
 
 /*
+ * vsa_tile_scores_noalloc - vsa_tile_scores for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). It takes no workspace: the double descriptors go to
+ * a fixed array of VSA_NOALLOC_SCRATCH_BYTES bytes that the library holds on
+ * each GPU it runs on until the process ends, and the (batch, head) pairs are
+ * pooled and scored in chunks that fit it. Same arguments, rules and results
+ * as vsa_tile_scores; no hipMalloc, hipFree or allocating call is made.
+ *
+ * Returns VSA_ERR_SIZE when the Q and K descriptors of one (batch, head),
+ * 2 * max_video_tiles * width * 8 bytes, exceed the array (not possible within
+ * VSA_MAX_VIDEO_TILES and VSA_MAX_PROJ). Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (two streams, two threads) race
+ * and must be serialized by the caller. Calls on one stream are ordered.
+ */
+#define VSA_NOALLOC_SCRATCH_BYTES (32ll << 20)
+VSA_API int vsa_tile_scores_noalloc(const vsa_problem *prob, int32_t mode,
+                                    int32_t proj_dim, const void *qt, const void *kt,
+                                    const int32_t *slot_to_token, const float *wq,
+                                    const float *wk, float *scores, void *stream);
+
+/*
  * vsa_select_topk - step 3: per (b, h, video query tile i), keep the k best
  * video key tiles: higher score first, lower tile index first among equal
  * scores (-0.0 equals +0.0); tile j is kept iff
