@@ -1,4 +1,6 @@
 """The seeded input generator: determinism and the stated recipe (CPU only)."""
+import dataclasses
+
 import numpy as np
 
 from workloads import WORKLOADS, Workload
@@ -53,3 +55,14 @@ def test_weights_shapes_and_scale():
     p = make_weights(WORKLOADS["4a"])
     assert p["proj_q"].shape == (24, 128, 32)
     assert not np.array_equal(p["proj_q"], p["proj_k"])
+
+
+def test_parallel_generation_matches_sequential(monkeypatch):
+    """Heads drawn in parallel threads give the same values as one thread."""
+    w = dataclasses.replace(WORKLOADS["1"], H=5)
+    monkeypatch.setenv("VSA_INPUT_THREADS", "4")
+    par = make_qkv(w)
+    monkeypatch.setenv("VSA_INPUT_THREADS", "1")
+    seq = make_qkv(w)
+    for a, b in zip(par, seq):
+        np.testing.assert_array_equal(a, b)

@@ -23,6 +23,9 @@ subset of heads can be regenerated on its own):
 
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 from .configs import Workload
@@ -98,10 +101,24 @@ def make_qkv(w: Workload, heads=None, batches=None, as_bf16_bits: bool = False):
     dt = np.uint16 if as_bf16_bits else np.float32
     shape = (len(batches), len(heads), w.N, w.d)
     q, k, v = (np.empty(shape, dtype=dt) for _ in range(3))
-    for bi, b in enumerate(batches):
-        for hi, h in enumerate(heads):
-            for dst, src in zip((q, k, v), head_qkv(w, b, h)):
-                dst[bi, hi] = bf16_bits(src) if as_bf16_bits else src
+
+    def fill(job):
+        bi, b, hi, h = job
+        for dst, src in zip((q, k, v), head_qkv(w, b, h)):
+            dst[bi, hi] = bf16_bits(src) if as_bf16_bits else src
+
+    jobs = [(bi, b, hi, h) for bi, b in enumerate(batches) for hi, h in enumerate(heads)]
+    # Every (batch, head) has its own random streams, so the heads are drawn
+    # in parallel threads (NumPy releases the GIL in its array kernels); the
+    # values do not depend on the thread count.
+    workers = min(len(jobs), int(os.environ.get("VSA_INPUT_THREADS", "0"))
+                  or min(16, os.cpu_count() or 1))
+    if workers <= 1:
+        for j in jobs:
+            fill(j)
+    else:
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(fill, jobs))
     return q, k, v
 
 
