@@ -7,9 +7,13 @@ in HBM: tile map + gather, tile scores, top-k selection and the sparse
 attention, all in the library's kernels. Prints ONE JSON line.
 
 value = effective TFLOP/s of the whole layer (4*d * real query-key pairs the
-attention visits / step time). The roofline object covers the dominant
-kernel (the bf16 attention), timed with events on the stream it runs on.
-The CPU baseline is the oracle on a bounded sample of the same workload.
+attention visits / step time). ms_per_step is the median of K steps, each
+timed with events on the stream the library launches on (the wall-clock
+mean of the same K steps is reported beside it). The roofline object covers
+the dominant kernel (the bf16 attention), timed the same way. The other
+workloads are reported beside the headline, each with the same library's
+dense path (sparsity 0) for the speed-up. The CPU baseline is the oracle on
+a bounded sample of the headline workload.
 """
 
 from __future__ import annotations
@@ -17,6 +21,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import platform
 import sys
 import time
 
@@ -27,6 +32,8 @@ if ROOT not in sys.path:
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 HBM_PEAK_GBS = 8000.0
+# Workloads reported beside the headline by default.
+DEFAULT_ALSO = "3b,2,4a,4b,5,3a-h3,3b-r2va,3a-fp8"
 
 
 def log(msg):
@@ -39,17 +46,19 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="3a")
-    ap.add_argument("--also", default="3b,3a-h3,3b-r2va,3a-fp8",
+    ap.add_argument("--also", default=DEFAULT_ALSO,
                     help="extra workloads reported beside, ',' list; a '-h3' suffix keeps "
                          "only heads 0-2 (one GPU's share of 24 heads over 8 GPUs); "
                          "'-r2va' runs the two-stream budget (32 reference tiles of the "
                          "reference-image segment and 32 video tiles per query tile); "
                          "'-fp8' runs the E4M3 attention variant (its gather also writes the "
-                         "E4M3 tiles)")
+                         "E4M3 tiles). Plain workloads also time their dense path.")
     ap.add_argument("--fp8", action="store_true",
                     help="with --profile-attn-only: run the E4M3 variant of the layer")
-    ap.add_argument("--dense-steps", type=int, default=2)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--dense-steps", type=int, default=5,
+                    help="timed steps of the headline's dense path")
+    ap.add_argument("--also-steps", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-recall", action="store_true",
                     help="skip the teacher tile-map recall measurement")
@@ -61,18 +70,50 @@ def parse():
     return ap.parse_args()
 
 
+_INPUTS = {}
+
+
+def device_inputs(w):
+    """Q, K, V of a workload on the device (bf16 or f32), drawn once per
+    (seed, shape) and shared by every case that needs them; a workload with
+    fewer heads takes the leading heads of a cached one (every head has its
+    own random streams)."""
+    import torch
+    from workloads.inputs import make_qkv
+    key = (w.seed, w.B, w.d, w.grid, tuple(w.prefix), w.dtype)
+    hit = _INPUTS.get(key)
+    if hit is not None and hit[0].shape[1] >= w.H:
+        return [x[:, : w.H].contiguous() if x.shape[1] > w.H else x for x in hit]
+    t0 = time.time()
+    bits = w.dtype == "bf16"
+    q, k, v = make_qkv(w, as_bf16_bits=bits)
+    dev = [torch.from_numpy(x).cuda() for x in (q, k, v)]
+    del q, k, v
+    if bits:
+        dev = [x.view(torch.bfloat16) for x in dev]
+    torch.cuda.synchronize()
+    log(f"[bench] inputs {w.name} ({w.H} heads) drawn in {time.time() - t0:.1f}s")
+    _INPUTS[key] = dev
+    return dev
+
+
+def drop_inputs():
+    import torch
+    _INPUTS.clear()
+    torch.cuda.empty_cache()
+
+
 class Case:
     """Library buffers and inputs for one workload, resident on the GPU."""
 
     def __init__(self, wname: str, sparsity=None, heads=None, ref=None, workload=None,
-                 inputs=None, fp8=False):
+                 fp8=False):
         import dataclasses
 
-        import numpy as np
         import torch
         from block_sparse_video_map_amd import vsa
         from workloads import WORKLOADS
-        from workloads.inputs import make_qkv, make_weights
+        from workloads.inputs import make_weights
         w = WORKLOADS[wname] if workload is None else workload
         if heads is not None:
             w = dataclasses.replace(w, H=heads)
@@ -85,17 +126,7 @@ class Case:
         self.fp8 = fp8
         self.layer = vsa.Layer(self.prob, self.sparsity, mode, proj, with_lse=False, ref=ref,
                                fp8=fp8)
-        t0 = time.time()
-        bits = w.dtype == "bf16"
-        if inputs is not None:                     # device tensors of another case
-            self.q, self.k, self.v = inputs
-        else:
-            q, k, v = make_qkv(w, as_bf16_bits=bits)
-            dev = [torch.from_numpy(x).cuda() for x in (q, k, v)]
-            del q, k, v
-            if bits:
-                dev = [x.view(torch.bfloat16) for x in dev]
-            self.q, self.k, self.v = dev
+        self.q, self.k, self.v = device_inputs(w)
         W = make_weights(w)
         if w.scorer == "mean_gate":
             self.wq, self.wk = torch.from_numpy(W["gate"]).cuda(), None
@@ -103,8 +134,6 @@ class Case:
             self.wq = torch.from_numpy(W["proj_q"]).cuda()
             self.wk = torch.from_numpy(W["proj_k"]).cuda()
         torch.cuda.synchronize()
-        log(f"[bench] {wname}: inputs ready in {time.time() - t0:.1f}s")
-        self._np = np
 
     def step(self):
         self.layer.forward(self.q, self.k, self.v, self.wq, self.wk)
@@ -126,18 +155,25 @@ class Case:
         return vsa.vsa_count_flops(self.prob, self.sparsity, s2t, kv)
 
     def time_steps(self, steps: int, warmup: int):
+        """(median ms from events around each step on the launch stream, wall
+        mean ms over the same steps)."""
         import torch
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         t0 = time.perf_counter()
-        for _ in range(steps):
+        ev[0].record()
+        for i in range(steps):
             self.step()
+            ev[i + 1].record()
         torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / steps
+        wall = (time.perf_counter() - t0) / steps * 1e3
+        ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+        return ms[len(ms) // 2], wall
 
     def stage_times(self, reps: int):
-        """Median ms per stage, from events on the launch stream."""
+        """Median and mean ms per stage, from events on the launch stream."""
         import torch
         L = self.layer
         names = ["map_gather", "scores", "select", "attention"]
@@ -188,6 +224,19 @@ class Case:
         torch.cuda.empty_cache()
 
 
+def dense_row(wname: str, steps: int, heads=None):
+    """The same library's dense path (sparsity 0) on the workload's inputs."""
+    c = Case(wname, sparsity=0.0, heads=heads)
+    f = c.flops()
+    ms, wall = c.time_steps(max(1, steps), 1)
+    _, mean = c.stage_times(max(1, min(steps, 3)))
+    c.release()
+    return {"ms_per_step": round(ms, 3), "ms_per_step_wall_mean": round(wall, 3),
+            "attention_ms": round(mean["attention"], 3), "steps": max(1, steps),
+            "effective_tflop": f / 1e12,
+            "effective_tflops_attention": f / mean["attention"] / 1e9}
+
+
 def teacher_recall(wname: str):
     """Tile recall of the mean-gate and the TripPool selections against the
     teacher tile map (full attention max-pooled per tile pair), both at the
@@ -202,8 +251,7 @@ def teacher_recall(wname: str):
     w = WORKLOADS[wname]
     other = "trippool" if w.scorer == "mean_gate" else "mean_gate"
     base = Case(wname)
-    alt = Case(wname, workload=dataclasses.replace(w, scorer=other),
-               inputs=(base.q, base.k, base.v))
+    alt = Case(wname, workload=dataclasses.replace(w, scorer=other))
     sels = {w.scorer: base, other: alt}
     for c in sels.values():
         c.step()
@@ -233,56 +281,91 @@ def teacher_recall(wname: str):
         out[name] = round(float(np.mean(rec)), 4)
     alt.release()
     base.release()
+    del lse, teacher
     out["teacher_map_ms"] = round(t_ms, 2)
     out["note"] = ("synthetic inputs, untrained gates/projections: a measurement of the "
                    "pipeline, not comparable to trained predictors")
     return out
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()
+                    if i.get("user_api") == "blas"] + [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
 def cpu_baseline(wname: str, budget_s: float):
-    """The oracle, as it stands, on a bounded sample of the workload: head 0's
-    map, gather, pooling, scores and selection, then attention for as many
-    video query tiles (plus every prefix query tile) as fit the time budget.
-    Reported as effective TFLOP/s of the sampled attention over the whole
-    sampled time."""
+    """The oracle, as it stands (float64 NumPy), on a bounded sample of the
+    workload: heads 0, 8 and 16, each with its full map, gather, pooling,
+    scores and selection and then attention for as many query tiles (every
+    prefix query tile first, then random video query tiles) as a third of
+    the time budget allows. Reported as effective TFLOP/s of the sampled
+    attention over the sampled time, and as milliseconds per layer
+    extrapolated from the sample (per head: the measured pre-attention time
+    plus the measured attention time per query tile times the head's query
+    tiles; summed over the layer's heads)."""
     import numpy as np
 
     import oracle
     from workloads import WORKLOADS
     from workloads.inputs import head_qkv, make_weights
     w = WORKLOADS[wname]
-    q, k, v = head_qkv(w, 0, 0)
     W = make_weights(w)
-    shape = w.tile_shapes[0]
-    wq = W["gate"][0] if w.scorer == "mean_gate" else W["proj_q"][0]
-    wk = None if w.scorer == "mean_gate" else W["proj_k"][0]
-    t0 = time.perf_counter()
-    r = oracle.head_forward(q, k, v, w.grid, w.prefix, shape, w.sparsity, w.scorer, wq, wk,
-                            query_tiles=[], tripool_mode=w.tripool_mode)
-    tm, allow = r["tmap"], r["allow"]
-    order = list(range(tm.n_prefix_tiles)) + list(
-        np.random.default_rng(0).permutation(np.arange(tm.n_prefix_tiles, tm.n_tiles)))
-    real = tm.valid().sum(axis=1).astype(np.int64)
-    done_flops, n_tiles = 0, 0
+    heads = [h for h in (0, 8, 16) if h < w.H] or [0]
+    per_head_budget = budget_s / len(heads)
     scale = 1.0 / np.sqrt(w.d)
-    for tq in order:
-        oracle.sparse_attention(q, k, v, tm, allow, scale, query_tiles=[tq])
-        done_flops += 4 * w.d * int(real[tq]) * int(allow[tq].astype(np.int64) @ real)
-        n_tiles += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    el = time.perf_counter() - t0
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
-    return {"value": done_flops / el / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+    done_flops, sampled_s, n_done, pre_s, tile_s, tiles_all = 0, 0.0, 0, [], [], []
+    for h in heads:
+        q, k, v = head_qkv(w, 0, h)
+        shape = w.tile_shapes[h % len(w.tile_shapes)]
+        wq = W["gate"][h] if w.scorer == "mean_gate" else W["proj_q"][h]
+        wk = None if w.scorer == "mean_gate" else W["proj_k"][h]
+        t0 = time.perf_counter()
+        r = oracle.head_forward(q, k, v, w.grid, w.prefix, shape, w.sparsity, w.scorer, wq,
+                                wk, query_tiles=[], tripool_mode=w.tripool_mode)
+        t_pre = time.perf_counter() - t0
+        tm, allow = r["tmap"], r["allow"]
+        order = list(range(tm.n_prefix_tiles)) + list(np.random.default_rng(h).permutation(
+            np.arange(tm.n_prefix_tiles, tm.n_tiles)))
+        real = tm.valid().sum(axis=1).astype(np.int64)
+        t1 = time.perf_counter()
+        n_tiles = 0
+        for tq in order:
+            oracle.sparse_attention(q, k, v, tm, allow, scale, query_tiles=[tq])
+            done_flops += 4 * w.d * int(real[tq]) * int(allow[tq].astype(np.int64) @ real)
+            n_tiles += 1
+            if time.perf_counter() - t0 > per_head_budget:
+                break
+        t_att = time.perf_counter() - t1
+        sampled_s += time.perf_counter() - t0
+        n_done += n_tiles
+        pre_s.append(t_pre)
+        tile_s.append(t_att / max(1, n_tiles))
+        tiles_all.append(tm.n_tiles)
+    per_head_ms = (np.mean(pre_s) + np.mean(tile_s) * np.mean(tiles_all)) * 1e3
+    return {"value": done_flops / sampled_s / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
             "kind": "oracle",
-            "sample": (f"workload {wname}, head 0 of {w.H}: full map/gather/pool/score/select "
-                       f"plus float64 attention of {n_tiles} of {tm.n_tiles} query tiles "
-                       f"(prefix tiles first, then random video tiles) in {el:.1f}s"),
-            "seconds": round(el, 2), "host_cpus": os.cpu_count()}
+            "sample": (f"workload {wname}, heads {heads} of {w.H}: full map/gather/pool/score/"
+                       f"select per head plus float64 attention of {n_done} query tiles "
+                       f"(each head's prefix tiles first, then random video tiles) in "
+                       f"{sampled_s:.1f}s"),
+            "ms_per_layer_extrapolated": round(per_head_ms * w.H * w.B, 1),
+            "seconds": round(sampled_s, 2), "cpu_model": cpu_model(),
+            "nproc": os.cpu_count(), "blas_threads": blas_threads()}
 
 
 def measured_peak(reps: int = 5) -> dict:
@@ -323,6 +406,44 @@ def measured_peak(reps: int = 5) -> dict:
     return out
 
 
+def also_row(label: str, steps: int):
+    """One workload reported beside the headline."""
+    from block_sparse_video_map_amd.profsum import read_traffic
+    name, heads, ref, sp, fp8 = label, None, None, None, False
+    if name.endswith("-fp8"):         # E4M3 attention variant (reduced precision)
+        name, fp8 = name[:-4], True
+    if name.endswith("-h3"):          # one GPU's share when 8 GPUs split the heads
+        name, heads = name[:-3], 3
+    if name.endswith("-r2va"):        # two-stream budget: 32 + 32 tiles per query tile
+        name, ref, sp = name[:-5], (1, 32), 0.9819
+    plain = not (fp8 or heads or ref)
+    c = Case(name, heads=heads, ref=ref, sparsity=sp, fp8=fp8)
+    f = c.flops()
+    ms, wall = c.time_steps(max(3, steps), 2)
+    med, mean = c.stage_times(5)
+    att = mean["attention"]
+    row = {"ms_per_step": round(ms, 4), "ms_per_step_wall_mean": round(wall, 4),
+           "effective_tflops_layer": f / ms / 1e9, "attention_ms": round(att, 4),
+           "effective_tflops_attention": f / att / 1e9, "effective_tflop": f / 1e12,
+           "stage_ms_median": med}
+    c.release()
+    if fp8:
+        row["precision"] = ("E4M3 Q/K/V and probabilities, fp32 accumulation, bf16 output: a "
+                            "reduced-precision variant, not the headline")
+        row["frac_of_fp8_peak"] = round(f / att / 1e9 / FP8_PEAK_TFLOPS, 4)
+        rec = read_traffic(os.path.join(ROOT, "profiles", f"attn_fp8_{name}_traffic.md"),
+                           "attn_fp8_kernel", name) if heads is None else None
+        row["traffic"] = rec["bytes_per_launch"] if rec else None
+    else:
+        row["roofline_frac"] = round(f / att / 1e9 / BF16_PEAK_TFLOPS, 4)
+    if plain:
+        big = c.w.N * c.w.H > 4_000_000
+        dense = dense_row(name, 1 if big else 3)
+        row["dense"] = dense
+        row["speedup_vs_dense_layer"] = round(dense["ms_per_step"] / ms, 3)
+    return row
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -353,7 +474,7 @@ def main():
         log("[bench] profile run done")
         return
     cold_ms = case.cold_ms
-    ms_step = case.time_steps(a.steps, a.warmup) * 1e3
+    ms_step, wall_step = case.time_steps(a.steps, a.warmup)
     med, mean = case.stage_times(max(5, a.steps))
     kept, frac = vsa.vsa_kept_stats(case.prob, case.sparsity)
     sbytes = case.stage_bytes()
@@ -362,47 +483,17 @@ def main():
                  for n, b in sbytes.items()}
     attn_ms = mean["attention"]
     achieved = flops / (attn_ms * 1e-3) / 1e12
-    log(f"[bench] {a.workload}: {ms_step:.3f} ms/step, attention {attn_ms:.3f} ms, "
-        f"{achieved:.1f} TFLOP/s on kept tiles")
+    log(f"[bench] {a.workload}: {ms_step:.3f} ms/step (event median), attention "
+        f"{attn_ms:.3f} ms, {achieved:.1f} TFLOP/s on kept tiles")
     case.release()
 
-    dense = Case(a.workload, sparsity=0.0)
-    dense_flops = dense.flops()
-    dense_ms = dense.time_steps(max(1, a.dense_steps), 1) * 1e3
-    dmed, dmean = dense.stage_times(max(1, a.dense_steps))
-    dense.release()
-    log(f"[bench] dense: {dense_ms:.2f} ms/step")
+    dense = dense_row(a.workload, a.dense_steps)
+    log(f"[bench] dense: {dense['ms_per_step']:.2f} ms/step")
 
     extra = {}
-    for name in [x for x in a.also.split(",") if x]:
-        heads, ref, sp, label, fp8 = None, None, None, name, False
-        if name.endswith("-fp8"):         # E4M3 attention variant (reduced precision)
-            name, fp8 = name[:-4], True
-        if name.endswith("-h3"):          # one GPU's share when 8 GPUs split the heads
-            name, heads = name[:-3], 3
-        if name.endswith("-r2va"):        # two-stream budget: 32 + 32 tiles per query tile
-            name, ref, sp = name[:-5], (1, 32), 0.9819
-        c = Case(name, heads=heads, ref=ref, sparsity=sp, fp8=fp8)
-        name = label
-        f = c.flops()
-        ms = c.time_steps(max(3, a.steps // 2), 2) * 1e3
-        m2, mn2 = c.stage_times(5)
-        extra[name] = {"ms_per_step": round(ms, 4), "effective_tflops_layer": f / ms / 1e9,
-                       "attention_ms": round(mn2["attention"], 4),
-                       "effective_tflops_attention": f / mn2["attention"] / 1e9,
-                       "effective_tflop": f / 1e12, "stage_ms_median": m2}
-        if fp8:
-            from block_sparse_video_map_amd.profsum import read_traffic
-            extra[name]["precision"] = ("E4M3 Q/K/V and probabilities, fp32 accumulation, "
-                                        "bf16 output: a reduced-precision variant, not the "
-                                        "headline")
-            extra[name]["frac_of_fp8_peak"] = round(f / mn2["attention"] / 1e9 / FP8_PEAK_TFLOPS,
-                                                    4)
-            rec = read_traffic(os.path.join(ROOT, "profiles", f"attn_fp8_{name[:-4]}_traffic.md"),
-                               "attn_fp8_kernel", name[:-4]) if heads is None else None
-            extra[name]["traffic"] = rec["bytes_per_launch"] if rec else None
-        c.release()
-        log(f"[bench] {name}: {ms:.3f} ms/step")
+    for label in [x for x in a.also.split(",") if x]:
+        extra[label] = also_row(label, a.also_steps)
+        log(f"[bench] {label}: {extra[label]['ms_per_step']:.3f} ms/step")
 
     log("[bench] matrix-core probe (measured-clock peak)")
     mpeak = measured_peak()
@@ -417,6 +508,7 @@ def main():
         log("[bench] teacher tile-map recall")
         recall = teacher_recall(a.workload)
         log(f"[bench] recall {recall}")
+    drop_inputs()
 
     cpu = None
     if not a.no_cpu_baseline:
@@ -436,6 +528,8 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_wall_mean": round(wall_step, 4),
+        "timing": "median of the steps, each bracketed by events on the launch stream",
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) + low-frequency 3D sinusoid per channel; "
@@ -462,10 +556,8 @@ def main():
         "stage_ms_mean": mean,
         "stage_hbm": stage_gbs,
         "kept_tile_pairs": kept, "kept_fraction_of_full": round(frac, 5),
-        "dense": {"ms_per_step": round(dense_ms, 3), "attention_ms": round(dmean["attention"], 3),
-                  "effective_tflop": dense_flops / 1e12,
-                  "effective_tflops_attention": dense_flops / dmean["attention"] / 1e9},
-        "speedup_vs_dense_layer": round(dense_ms / ms_step, 3),
+        "dense": dense,
+        "speedup_vs_dense_layer": round(dense["ms_per_step"] / ms_step, 3),
         "also": extra,
         "teacher_recall": recall,
     }
