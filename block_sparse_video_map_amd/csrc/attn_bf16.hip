@@ -264,6 +264,22 @@ void attn_bf16_kernel(Plan p, PairGrid gd, const bf16_bits *__restrict__ qt,
 
   if (threadIdx.x < kSplits * 4) grp_count[threadIdx.x] = 0;
   if (threadIdx.x == 0) fault = 0;
+  // A wave whose tile has no unit in a paired step (entry kNone) still runs
+  // its PV products, with every probability zero, on its tile's half of the
+  // V slot, which this kernel may not have written yet. LDS keeps what an
+  // earlier kernel left there, possibly NaN or Inf bit patterns, and
+  // 0 * NaN = NaN; so the V rings start zeroed (whatever the kernel writes
+  // there later is a finite V row). The barriers of the list building order
+  // these stores before the first copy into the rings.
+  {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    u32x4 *v0 = reinterpret_cast<u32x4 *>(vslot0), *v1 = reinterpret_cast<u32x4 *>(vslot1);
+    for (int x = threadIdx.x; x < kSplits * SLOT / 8; x += kThreads) {
+      v0[x] = z;
+      v1[x] = z;
+    }
+  }
 
   bf16x8 qf[NC];
   const int qtile = myT >= 0 ? myT : tA;
