@@ -182,6 +182,9 @@ class Case:
                L.select, L.attend]
         if self.sparsity == 0.0:
             names, fns = [names[0], names[3]], [fns[0], fns[3]]
+        elif L.fused:                      # pooling, scores and top-k in one call
+            names = [names[0], "score_select", names[3]]
+            fns = [fns[0], lambda: L.score_select(self.wq, self.wk), fns[3]]
         if self.fp8:                       # the gather writes the E4M3 tiles too
             names[0] = "map_gather_fp8"
             fns[0] = lambda: L.map_tiles_fp8(self.q, self.k, self.v)
@@ -199,6 +202,42 @@ class Case:
         mean = {n: float(sum(v) / len(v)) for n, v in samples.items()}
         return med, mean
 
+    def fused_select_ms(self, reps: int = 5):
+        """Median ms of vsa_tile_select (pooling, scores and top-k in one call,
+        no score matrix) beside the two calls it replaces, on this layer's
+        tiles; None where the call does not take the problem."""
+        import torch
+        from block_sparse_video_map_amd import vsa
+        L = self.layer
+        if self.sparsity == 0.0 or not vsa.fused_select_supported(
+                self.prob, L.mode, L.proj_dim, self.sparsity):
+            return None
+        kv = torch.empty_like(L.kv_idx)
+
+        def fused():
+            vsa.vsa_tile_select(self.prob, L.mode, L.proj_dim, L.qt, L.kt, L.slot_to_token,
+                                self.wq, self.wk, self.sparsity, L.pooled, kv)
+
+        def two():
+            L.tile_scores(self.wq, self.wk)
+            L.select()
+        out = {}
+        for name, fn in (("fused_call", fused), ("two_calls", two)):
+            fn()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(reps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b))
+            out[name + "_ms"] = round(sorted(ts)[len(ts) // 2], 4)
+        out["lists_equal"] = bool(torch.equal(kv[: L.sizes.idx_elems],
+                                              L.kv_idx[: L.sizes.idx_elems]))
+        return out
+
     def stage_bytes(self) -> dict:
         """Algorithmic HBM bytes of the HBM-bound stages (each input read and
         each output written once)."""
@@ -213,7 +252,10 @@ class Case:
         nstat = {"triplet": 3, "maxmin": 2, "avg": 1}[w.tripool_mode]
         r = w.d if w.scorer == "mean_gate" else nstat * w.proj_dim
         out = {"map_gather": 3 * es * w.B * w.H * w.N * w.d + 3 * es * tiles * 64 * w.d}
-        if self.sparsity != 0.0:
+        if self.sparsity != 0.0 and self.layer.fused:
+            # tiles read by the pooling, descriptors written and read back, lists written
+            out["score_select"] = 2 * es * vt * 64 * w.d + 4 * 8 * vt * r + 4 * kk
+        elif self.sparsity != 0.0:
             out["scores"] = 2 * es * vt * 64 * w.d + 2 * 8 * vt * r + 4 * vt2
             out["select"] = 4 * vt2 + 4 * kk
         return out
@@ -426,6 +468,8 @@ def also_row(label: str, steps: int):
            "effective_tflops_layer": f / ms / 1e9, "attention_ms": round(att, 4),
            "effective_tflops_attention": f / att / 1e9, "effective_tflop": f / 1e12,
            "stage_ms_median": med}
+    if plain:
+        row["fused_select"] = c.fused_select_ms()
     c.release()
     if fp8:
         row["precision"] = ("E4M3 Q/K/V and probabilities, fp32 accumulation, bf16 output: a "
@@ -485,6 +529,7 @@ def main():
     achieved = flops / (attn_ms * 1e-3) / 1e12
     log(f"[bench] {a.workload}: {ms_step:.3f} ms/step (event median), attention "
         f"{attn_ms:.3f} ms, {achieved:.1f} TFLOP/s on kept tiles")
+    fused_sel = case.fused_select_ms()
     case.release()
 
     dense = dense_row(a.workload, a.dense_steps)
@@ -553,6 +598,7 @@ def main():
         "attention_ms": round(attn_ms, 4),
         "cold_ms_first_step": round(cold_ms, 3),
         "stage_ms_median": med,
+        "fused_select": fused_sel,
         "stage_ms_mean": mean,
         "stage_hbm": stage_gbs,
         "kept_tile_pairs": kept, "kept_fraction_of_full": round(frac, 5),

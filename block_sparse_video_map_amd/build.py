@@ -24,7 +24,7 @@ LIB = os.path.join(PKG, "libvsa.so")
 
 SOURCES = ["plan.cpp", "abi.hip", "map_gather.hip", "pool_score.hip", "select.hip",
            "attn_bf16.hip", "attn_f32.hip", "teacher.hip", "quant_fp8.hip", "attn_fp8.hip",
-           "probe.hip", "scores_noalloc.hip"]
+           "probe.hip", "scores_noalloc.hip", "score_select.hip"]
 # Per-source extra flags (none needed at present).
 EXTRA: dict = {}
 ARCH = "gfx950"

@@ -133,6 +133,48 @@ VSA_API int vsa_select_topk(const vsa_problem *prob, const float *scores, double
   return hip_status(launch_select(p, j, (hipStream_t)stream));
 }
 
+VSA_API int vsa_tile_select(const vsa_problem *prob, int32_t mode, int32_t proj_dim,
+                            const void *qt, const void *kt, const int32_t *slot_to_token,
+                            const float *wq, const float *wk, double sparsity, void *pooled_ws,
+                            int32_t *kv_idx, void *stream) {
+  Plan p;
+  int st = make_plan(prob, sparsity, &p);
+  if (st != VSA_OK) return st;
+  int64_t bytes = 0;
+  st = vsa_pooled_bytes(prob, mode, proj_dim, &bytes);
+  if (st != VSA_OK) return st;
+  if (p.dense) return VSA_ERR_INVALID_ARG;            // nothing to select
+  if (!qt || !kt || !slot_to_token || !wq || !pooled_ws || !kv_idx) return VSA_ERR_INVALID_ARG;
+  if (mode != VSA_SCORE_MEAN_GATE && !wk) return VSA_ERR_INVALID_ARG;
+  if (!aligned16(qt) || !aligned16(kt) || ((uintptr_t)pooled_ws & 7u))
+    return VSA_ERR_INVALID_ARG;
+  int r = 0;
+  descriptor_width(mode, proj_dim, p.d, &r);         // validated by vsa_pooled_bytes
+  if (p.max_vt > VSA_FUSED_MAX_TILES || r % 32 != 0 || r > VSA_FUSED_MAX_R)
+    return VSA_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  PoolJob job;
+  job.tile0 = p.n_prefix_tiles;
+  job.ntiles = -1;
+  job.rows = p.max_vt;
+  job.src[0] = qt;
+  job.src[1] = kt;
+  job.w[0] = wq;
+  job.w[1] = (mode == VSA_SCORE_MEAN_GATE && !wk) ? wq : wk;
+  hipError_t e = launch_pool(p, mode, proj_dim, job, 2, slot_to_token, (double *)pooled_ws, s);
+  if (e != hipSuccess) return VSA_ERR_HIP;
+  const int64_t bh = (int64_t)p.B * p.H;
+  FusedSelectJob fj;
+  fj.q = (const double *)pooled_ws;
+  fj.q_bh = (int64_t)p.max_vt * r;
+  fj.k = (const double *)pooled_ws + bh * p.max_vt * r;
+  fj.k_bh = (int64_t)p.max_vt * r;
+  fj.out = kv_idx;
+  fj.out_row = p.k_max;
+  fj.out_bh = (int64_t)p.max_vt * p.k_max;
+  return hip_status(launch_score_select(p, r, fj, s));
+}
+
 VSA_API int vsa_sparse_attn_fwd(const vsa_problem *prob, const void *qt, const void *kt,
                                 const void *vt, const int32_t *slot_to_token,
                                 const int32_t *kv_idx, double sparsity,

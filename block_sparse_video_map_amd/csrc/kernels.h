@@ -60,10 +60,26 @@ struct SelectJob {
   int64_t out_bh;
 };
 
+// Fused scores and top-k: descriptors q (rows) and k (columns) per
+// (batch*head), q_bh / k_bh doubles apart; the ascending lists go to
+// out[bh*out_bh + i*out_row], padded with -1 up to out_row.
+struct FusedSelectJob {
+  const double *q;
+  int64_t q_bh;
+  const double *k;
+  int64_t k_bh;
+  int32_t *out;
+  int32_t out_row;
+  int64_t out_bh;
+};
+
 hipError_t launch_pool(const Plan &p, int mode, int proj_dim, const PoolJob &job, int nsrc,
                        const int32_t *s2t, double *pooled, hipStream_t stream);
 hipError_t launch_scores(const Plan &p, int r, const ScoreJob &job, hipStream_t stream);
 hipError_t launch_select(const Plan &p, const SelectJob &job, hipStream_t stream);
+// Needs p.max_vt <= VSA_FUSED_MAX_TILES and r % 32 == 0, r <= VSA_FUSED_MAX_R.
+hipError_t launch_score_select(const Plan &p, int r, const FusedSelectJob &job,
+                               hipStream_t stream);
 // ref_idx: the reference stream's kept tiles when p.n_ref > 0, else unused.
 hipError_t launch_attention(const Plan &p, const void *qt, const void *kt,
                             const void *vt, const int32_t *s2t, const int32_t *kv_idx,

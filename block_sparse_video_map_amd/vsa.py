@@ -26,11 +26,13 @@ VSA_SCORE_TRIPPOOL_MAXMIN, VSA_SCORE_TRIPPOOL_AVG = 2, 3
 VSA_TILE, VSA_MAX_SEGMENTS, VSA_MAX_SHAPES = 64, 8, 16
 VSA_MAX_VIDEO_TILES, VSA_MAX_PROJ, VSA_MAX_TILES = 8192, 64, 16383
 VSA_NOALLOC_SCRATCH_BYTES = 32 << 20     # fixed device array of vsa_tile_scores_noalloc
+VSA_FUSED_MAX_TILES = 4096               # vsa_tile_select: video tiles per head
+VSA_FUSED_MAX_R = 192                    # vsa_tile_select: descriptor width (doubles)
 
 # Names declared in include/vsa.h.
 EXPORTS = ("vsa_query_sizes", "vsa_pooled_bytes", "vsa_map_tiles", "vsa_tile_scores",
            "vsa_tile_scores_noalloc",
-           "vsa_select_topk", "vsa_sparse_attn_fwd", "vsa_kept_stats",
+           "vsa_select_topk", "vsa_tile_select", "vsa_sparse_attn_fwd", "vsa_kept_stats",
            "vsa_count_flops", "vsa_ref_sizes", "vsa_ref_pooled_bytes", "vsa_ref_scores",
            "vsa_ref_select", "vsa_sparse_attn_fwd_ref", "vsa_kept_stats_ref",
            "vsa_count_flops_ref", "vsa_teacher_map", "vsa_quantize_fp8", "vsa_map_tiles_fp8",
@@ -93,6 +95,7 @@ def lib() -> ctypes.CDLL:
             "vsa_tile_scores": [P, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp],
             "vsa_tile_scores_noalloc": [P, i32, i32, vp, vp, vp, vp, vp, vp, vp],
             "vsa_select_topk": [P, vp, f64, vp, vp],
+            "vsa_tile_select": [P, i32, i32, vp, vp, vp, vp, vp, f64, vp, vp, vp],
             "vsa_sparse_attn_fwd": [P, vp, vp, vp, vp, vp, f64, f32, vp, vp, vp],
             "vsa_kept_stats": [P, f64, ctypes.POINTER(i64), ctypes.POINTER(f64)],
             "vsa_count_flops": [P, f64, vp, vp, ctypes.POINTER(f64)],
@@ -295,6 +298,31 @@ def vsa_select_topk(prob: Problem, scores, sparsity: float, kv_idx, stream=None)
     _need(kv_idx, sz.idx_elems, torch.int32, "kv_idx")
     _check("vsa_select_topk", lib().vsa_select_topk(
         prob.ref, _ptr(scores), float(sparsity), _ptr(kv_idx), _stream(stream)))
+
+
+def fused_select_supported(prob: Problem, mode: int, proj_dim: int, sparsity: float) -> bool:
+    """Whether vsa_tile_select takes this problem (host-side check, no HIP call)."""
+    if sparsity == 0.0:
+        return False
+    sz = vsa_query_sizes(prob, sparsity)
+    r = vsa_pooled_bytes(prob, mode, proj_dim) // (8 * sz.pooled_rows)
+    return (sz.max_video_tiles <= VSA_FUSED_MAX_TILES and r % 32 == 0
+            and r <= VSA_FUSED_MAX_R)
+
+
+def vsa_tile_select(prob: Problem, mode: int, proj_dim: int, qt, kt, slot_to_token, wq, wk,
+                    sparsity: float, pooled_ws, kv_idx, stream=None):
+    """Pooling, scores and top-k in one call; the score matrix is never written."""
+    import torch
+    sz = vsa_query_sizes(prob, sparsity)
+    _need(kv_idx, sz.idx_elems, torch.int32, "kv_idx")
+    _need(wq, 1, torch.float32, "wq")
+    _need(wk, 1, torch.float32, "wk")
+    if pooled_ws.numel() * pooled_ws.element_size() < vsa_pooled_bytes(prob, mode, proj_dim):
+        raise ValueError("pooled_ws too small")
+    _check("vsa_tile_select", lib().vsa_tile_select(
+        prob.ref, int(mode), int(proj_dim), _ptr(qt), _ptr(kt), _ptr(slot_to_token), _ptr(wq),
+        _ptr(wk), float(sparsity), _ptr(pooled_ws), _ptr(kv_idx), _stream(stream)))
 
 
 def vsa_sparse_attn_fwd(prob: Problem, qt, kt, vt, slot_to_token, kv_idx, sparsity: float,
@@ -517,9 +545,14 @@ class Layer:
 
     def __init__(self, prob: Problem, sparsity: float, mode: int, proj_dim: int,
                  device="cuda", with_lse: bool = True, ref: Optional[Tuple[int, int]] = None,
-                 fp8: bool = False):
+                 fp8: bool = False, fused: bool = False):
         import torch
         self.prob, self.sparsity, self.mode, self.proj_dim = prob, sparsity, mode, proj_dim
+        # fused=True: forward() scores and selects in one call (vsa_tile_select),
+        # which needs no score matrix but is slower than the two calls.
+        if fused and not fused_select_supported(prob, mode, proj_dim, sparsity):
+            raise ValueError("vsa_tile_select does not take this problem")
+        self.fused = bool(fused)
         self.sizes = sz = vsa_query_sizes(prob, sparsity)
         et = _elem_dtype(prob)
         dev = torch.device(device)
@@ -575,6 +608,19 @@ class Layer:
         if self.budget is not None:
             vsa_ref_select(self.prob, self.budget, self.ref_scores, self.ref_idx, stream)
 
+    def score_select(self, wq, wk, stream=None):
+        """Scores and top-k in one call (vsa_tile_select); the score matrix
+        is left unwritten. The two-stream budget's reference scores and
+        selection run as separate calls."""
+        vsa_tile_select(self.prob, self.mode, self.proj_dim, self.qt, self.kt,
+                        self.slot_to_token, wq, wk, self.sparsity, self.pooled, self.kv_idx,
+                        stream)
+        if self.budget is not None:
+            vsa_ref_scores(self.prob, self.mode, self.proj_dim, self.kt, self.slot_to_token, wq,
+                           wk, self.budget, self.pooled, self.ref_pooled, self.ref_scores,
+                           stream)
+            vsa_ref_select(self.prob, self.budget, self.ref_scores, self.ref_idx, stream)
+
     def attend(self, softmax_scale: float = 0.0, stream=None, kv_idx=None, ref_idx=None):
         kv = self.kv_idx if kv_idx is None else kv_idx
         if self.fp8:
@@ -598,14 +644,18 @@ class Layer:
 
     def forward(self, q, k, v, wq, wk, softmax_scale: float = 0.0, stream=None):
         """One whole layer: map+gather, scores, top-k, attention (fp8: the
-        gather also writes the E4M3 tiles)."""
+        gather also writes the E4M3 tiles). Scores and top-k are one call
+        (vsa_tile_select) when self.fused."""
         if self.fp8:
             self.map_tiles_fp8(q, k, v, stream)
         else:
             self.map_tiles(q, k, v, stream)
         if self.sparsity != 0.0:
-            self.tile_scores(wq, wk, stream)
-            self.select(stream)
+            if self.fused:
+                self.score_select(wq, wk, stream)
+            else:
+                self.tile_scores(wq, wk, stream)
+                self.select(stream)
         self.attend(softmax_scale, stream)
         return self.out
 

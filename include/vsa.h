@@ -231,6 +231,31 @@ VSA_API int vsa_select_topk(const vsa_problem *prob, const float *scores,
                             double sparsity, int32_t *kv_idx, void *stream);
 
 /*
+ * vsa_tile_select - steps 2 and 3 in one call: the pooled descriptors of
+ * vsa_tile_scores, then the top-k of vsa_select_topk, without writing the
+ * score matrix (the pages' engine keeps its intermediates bounded by working
+ * in chunks: "BSAI-ComfyUI-VedaSparse" README, Implementation section). Each
+ * score is the same double dot product, accumulated in the same order and
+ * rounded once to float, so kv_idx equals that of vsa_tile_scores followed
+ * by vsa_select_topk.
+ *
+ * Arguments as vsa_tile_scores (pooled_ws: device, vsa_pooled_bytes bytes,
+ * overwritten) plus sparsity (> 0) and kv_idx (device) of vsa_select_topk.
+ * Needs max_video_tiles <= VSA_FUSED_MAX_TILES and a descriptor width that is
+ * a multiple of 32 and at most VSA_FUSED_MAX_R: the mean gate with d = 64 or
+ * 128; TripPool with proj_dim 32 or 64 (any mode) or 16 (maxmin). Otherwise
+ * returns VSA_ERR_UNSUPPORTED before any launch; the two separate calls cover
+ * every size.
+ */
+#define VSA_FUSED_MAX_TILES 4096
+#define VSA_FUSED_MAX_R 192
+VSA_API int vsa_tile_select(const vsa_problem *prob, int32_t mode,
+                            int32_t proj_dim, const void *qt, const void *kt,
+                            const int32_t *slot_to_token, const float *wq,
+                            const float *wk, double sparsity, void *pooled_ws,
+                            int32_t *kv_idx, void *stream);
+
+/*
  * vsa_sparse_attn_fwd - step 4: for every real query token t,
  *   O_t = softmax_u(q_t . k_u * scale) V_u over its allowed real keys u.
  * A video query tile is allowed every prefix tile and its kv_idx video

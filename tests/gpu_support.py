@@ -158,6 +158,41 @@ def run_library(w: Workload, sparsity=None, stages=("map", "score", "select", "a
     return GpuRun(w, prob, layer, q, k, v, wq, wk)
 
 
+def fused_kv(run: GpuRun, sparsity=None):
+    """kv_idx from vsa_tile_select (pooling, scores and top-k in one call) on
+    the run's tiled copies, or None when the call does not take the problem."""
+    import torch
+    from block_sparse_video_map_amd import vsa
+    w, L = run.w, run.layer
+    sp = w.sparsity if sparsity is None else sparsity
+    if not vsa.fused_select_supported(run.prob, L.mode, L.proj_dim, sp):
+        return None
+    kv = torch.full_like(L.kv_idx, -7)
+    pooled = torch.empty_like(L.pooled)
+    vsa.vsa_tile_select(run.prob, L.mode, L.proj_dim, L.qt, L.kt, L.slot_to_token, run.wq,
+                        run.wk, sp, pooled, kv)
+    torch.cuda.synchronize()
+    return kv
+
+
+def assert_fused_equal(run: GpuRun, sparsity=None):
+    """The fused call's lists equal the two-call path's (vsa_tile_scores then
+    vsa_select_topk), row for row over every head's video query tiles."""
+    kvf = fused_kv(run, sparsity)
+    if kvf is None:
+        log(f"[fused] {run.w.name}: problem not taken by vsa_tile_select")
+        return False
+    sz = run.layer.sizes
+    shape = (run.w.B * run.w.H, sz.max_video_tiles, sz.k_max)
+    a = run.layer.kv_idx[: sz.idx_elems].view(shape).cpu().numpy()
+    b = kvf[: sz.idx_elems].view(shape).cpu().numpy()
+    for bh in range(shape[0]):
+        n = sz.n_video_tiles[(bh % run.w.H) % len(run.w.tile_shapes)]
+        np.testing.assert_array_equal(b[bh, :n], a[bh, :n])
+    log(f"[fused] {run.w.name}: vsa_tile_select lists equal the two-call path's")
+    return True
+
+
 def tensor_f32(t) -> np.ndarray:
     import torch
     if t.dtype == torch.bfloat16:

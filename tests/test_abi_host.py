@@ -450,3 +450,43 @@ def test_count_flops_matches_oracle_on_random_geometries(T, Hv, Wv, prefix, shap
         kv[h, : tm.n_video_tiles, :k] = sel
         want += oracle.effective_flops(tm, oracle.allowed_tiles(tm, sel), 64)
     assert vsa.vsa_count_flops(p, sparsity, s2t, kv) == want
+
+
+def test_fused_select_rejects_before_launch():
+    """vsa_tile_select: argument errors and the sizes it does not take come
+    back before any launch (fake pointers, never dereferenced)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host-only check; skipped where a GPU is visible")
+    L = vsa.lib()
+    fake = ctypes.c_void_p(0x10000)
+    p = _problem(WORKLOADS["1"])
+    call = lambda prob, mode, proj, sp, **kw: L.vsa_tile_select(
+        prob.ref, mode, proj, kw.get("qt", fake), fake, fake, fake, kw.get("wk", fake), sp,
+        fake, kw.get("kv", fake), None)
+    assert call(p, 0, p.d, 0.0) == vsa.VSA_ERR_INVALID_ARG          # dense: nothing to select
+    assert call(p, 0, p.d, 0.75, kv=None) == vsa.VSA_ERR_INVALID_ARG
+    assert call(p, 0, p.d, 0.75, qt=None) == vsa.VSA_ERR_INVALID_ARG
+    assert call(p, 1, 32, 0.75, wk=None) == vsa.VSA_ERR_INVALID_ARG
+    # descriptor width 24 (TripPool, proj 8) is not a multiple of 32
+    assert call(p, 1, 8, 0.75) == vsa.VSA_ERR_UNSUPPORTED
+    # 48 = TripPool with proj 16; maxmin with proj 16 is 32 wide and taken
+    assert call(p, vsa.VSA_SCORE_TRIPPOOL, 16, 0.75) == vsa.VSA_ERR_UNSUPPORTED
+    big = vsa.Problem(1, 1, 128, (1, 1, 64 * (vsa.VSA_FUSED_MAX_TILES + 1)), (),
+                      ((1, 1, 64),), "bf16")
+    assert call(big, 0, 128, 0.75) == vsa.VSA_ERR_UNSUPPORTED
+
+
+def test_fused_select_support_rule():
+    """The binding's host-side rule matches the header's limits."""
+    w5, w1 = WORKLOADS["5"], WORKLOADS["1"]
+    assert vsa.fused_select_supported(_problem(w5), vsa.VSA_SCORE_TRIPPOOL, 32, 0.95)
+    assert not vsa.fused_select_supported(_problem(w5), vsa.VSA_SCORE_TRIPPOOL, 32, 0.0)
+    assert not vsa.fused_select_supported(_problem(w1), vsa.VSA_SCORE_TRIPPOOL, 8, 0.75)
+    assert vsa.fused_select_supported(_problem(w1), vsa.VSA_SCORE_TRIPPOOL_MAXMIN, 16, 0.75)
+    assert vsa.fused_select_supported(_problem(w1, d=64), vsa.VSA_SCORE_MEAN_GATE, 64, 0.5)
+    n = vsa.VSA_FUSED_MAX_TILES
+    ok = vsa.Problem(1, 1, 128, (1, 1, 64 * n), (), ((1, 1, 64),), "bf16")
+    too = vsa.Problem(1, 1, 128, (1, 1, 64 * (n + 1)), (), ((1, 1, 64),), "bf16")
+    assert vsa.fused_select_supported(ok, vsa.VSA_SCORE_MEAN_GATE, 128, 0.9)
+    assert not vsa.fused_select_supported(too, vsa.VSA_SCORE_MEAN_GATE, 128, 0.9)

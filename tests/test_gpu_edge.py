@@ -28,6 +28,10 @@ EDGE = {
     "proj64-many-shapes": Workload("edge-p64", "bf16", 1, 4, 128, (8, 8, 16), (5, 64, 1),
                                    ((4, 4, 4), (8, 4, 2), (2, 4, 8), (4, 8, 2)),
                                    "trippool", 0.75, 2006, proj_dim=64),
+    # the ragged head-aware case at a descriptor width the fused select takes
+    "ragged-headaware-b2-p32": Workload("edge-ragged32", "bf16", 2, 3, 128, (5, 12, 10),
+                                        (7, 0, 70), HEAD_AWARE_CYCLE, "trippool", 0.7, 2010,
+                                        proj_dim=32),
 }
 
 
@@ -91,6 +95,7 @@ def test_edge_workload_full_parity(name):
                 np.testing.assert_array_equal(gs.unpack_tiles(flat, tm.n_tiles, w.d, col),
                                               oracle.gather(x, tm))
     _full_check(w, run)
+    gs.assert_fused_equal(run)
 
 
 def test_dense_path_equals_dense_attention():
@@ -135,6 +140,7 @@ def test_exact_ties_go_to_lower_index():
         for row in got:      # never a later duplicate without the earlier one
             assert not (3 in row or 6 in row) or 1 in row
             assert 7 not in row or 0 in row
+    assert gs.assert_fused_equal(run)
 
 
 def test_deterministic_and_batch_independent():

@@ -123,6 +123,14 @@ def test_select_topk_bit_exact(run):
         assert differ <= wide
 
 
+def test_fused_select_equals_two_calls(run):
+    """vsa_tile_select (scores and top-k in one kernel, no score matrix)
+    returns exactly the lists of vsa_tile_scores + vsa_select_topk, which the
+    band rule above checks against the oracle."""
+    gs.log(f"[parity] fused select {run.name}")
+    assert gs.assert_fused_equal(run), "every workload is within vsa_tile_select's limits"
+
+
 def _pick_tiles(tm, count, seed):
     if count is None:
         return list(range(tm.n_tiles))

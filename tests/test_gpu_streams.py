@@ -14,12 +14,12 @@ B = Workload("st-b", "bf16", 2, 3, 128, (4, 12, 24), (100, 700, 30), HEAD_AWARE_
              "trippool", 0.8, 4402)
 
 
-def _layer(w, fp8):
+def _layer(w, fp8, fused=False):
     import torch
     from block_sparse_video_map_amd import vsa
     from workloads.inputs import make_weights
     layer = vsa.Layer(gs.problem_of(w), w.sparsity, vsa.score_mode(w.scorer, w.tripool_mode),
-                      w.d if w.scorer == "mean_gate" else w.proj_dim, fp8=fp8)
+                      w.d if w.scorer == "mean_gate" else w.proj_dim, fp8=fp8, fused=fused)
     W = make_weights(w)
     if w.scorer == "mean_gate":
         weights = (torch.from_numpy(W["gate"]).cuda(), None)
@@ -28,11 +28,15 @@ def _layer(w, fp8):
     return layer, gs.to_device(w), weights
 
 
-@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
-def test_two_streams_match_sequential_runs(fp8):
+@pytest.mark.parametrize("fp8,fused", [(False, False), (True, False), (False, True)],
+                         ids=["bf16", "fp8", "bf16-fused-select"])
+def test_two_streams_match_sequential_runs(fp8, fused):
+    """The fused case also guards the bf16 attention kernel against stale LDS:
+    its V rings must not feed bytes another kernel left there (possibly NaN
+    patterns) into the products of a step without a unit."""
     import torch
-    la, ia, wa = _layer(A, fp8)
-    lb, ib, wb = _layer(B, fp8)
+    la, ia, wa = _layer(A, fp8, fused)
+    lb, ib, wb = _layer(B, fp8, fused)
     la.forward(*ia, *wa)
     lb.forward(*ib, *wb)
     torch.cuda.synchronize()
@@ -48,6 +52,6 @@ def test_two_streams_match_sequential_runs(fp8):
             lb.forward(*ib, *wb)
     torch.cuda.synchronize()
     got = [la.out, la.lse, lb.out, lb.lse]
-    gs.log(f"[streams] fp8={fp8}: comparing {len(got)} buffers")
+    gs.log(f"[streams] fp8={fp8} fused={fused}: comparing {len(got)} buffers")
     for r, g in zip(ref, got):
         assert torch.equal(r, g)
