@@ -185,6 +185,10 @@ class Case:
         elif L.fused:                      # pooling, scores and top-k in one call
             names = [names[0], "score_select", names[3]]
             fns = [fns[0], lambda: L.score_select(self.wq, self.wk), fns[3]]
+        elif L.gather_pool:                # gather with the tile means, gate, scores
+            names = ["map_gather_scores", names[2], names[3]]
+            fns = [lambda: L.map_tiles_scores(self.q, self.k, self.v, self.wq, self.wk),
+                   fns[2], fns[3]]
         if self.fp8:                       # the gather writes the E4M3 tiles too
             names[0] = "map_gather_fp8"
             fns[0] = lambda: L.map_tiles_fp8(self.q, self.k, self.v)
@@ -252,7 +256,13 @@ class Case:
         nstat = {"triplet": 3, "maxmin": 2, "avg": 1}[w.tripool_mode]
         r = w.d if w.scorer == "mean_gate" else nstat * w.proj_dim
         out = {"map_gather": 3 * es * w.B * w.H * w.N * w.d + 3 * es * tiles * 64 * w.d}
-        if self.sparsity != 0.0 and self.layer.fused:
+        if self.sparsity != 0.0 and self.layer.gather_pool:
+            # the gather, then descriptors written, gated in place and read by the scores
+            out.pop("map_gather")
+            out["map_gather_scores"] = (3 * es * w.B * w.H * w.N * w.d + 3 * es * tiles * 64 * w.d
+                                        + 4 * 8 * vt * r + 4 * vt2)
+            out["select"] = 4 * vt2 + 4 * kk
+        elif self.sparsity != 0.0 and self.layer.fused:
             # tiles read by the pooling, descriptors written and read back, lists written
             out["score_select"] = 2 * es * vt * 64 * w.d + 4 * 8 * vt * r + 4 * kk
         elif self.sparsity != 0.0:

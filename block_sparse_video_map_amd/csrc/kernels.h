@@ -8,10 +8,18 @@
 
 hipError_t launch_build_map(const Plan &p, int32_t *s2t, hipStream_t stream);
 // q8/k8/v8/scales non-null (bf16 only): also the E4M3 copies and scale bytes
-// that launch_quant_fp8 would write, from the same pass.
+// that launch_quant_fp8 would write, from the same pass. means non-null: also
+// the channel means of the Q and K video tiles, double, at row
+// (which * B*H + bh) * max_vt + video tile (the pooling workspace's layout).
 hipError_t launch_gather(const Plan &p, const void *q, const void *k, const void *v,
                          const int32_t *s2t, void *qt, void *kt, void *vt, uint8_t *q8,
-                         uint8_t *k8, uint8_t *v8, uint8_t *scales, hipStream_t stream);
+                         uint8_t *k8, uint8_t *v8, uint8_t *scales, hipStream_t stream,
+                         double *means = nullptr);
+// Mean gate from the tile means launch_gather wrote into `pooled`: each row
+// is replaced, in place, by its product with the head's gate (wq for Q rows,
+// wk for K rows), as the mean-gate pooling kernel computes it.
+hipError_t launch_gate_means(const Plan &p, const float *wq, const float *wk, double *pooled,
+                             hipStream_t stream);
 // Tiles to pool: per (batch*head), tiles tile0 .. tile0+ntiles-1 of the tiled
 // copies (ntiles < 0: the head's video tiles); source z of the launch reads
 // src[z] with weights w[z] and writes rows ((z*nbh + bh - bh0)*rows + i) of

@@ -5,7 +5,11 @@
 // written out in the tiled operand layout as contiguous 16-byte vectors, so
 // both the HBM reads and the HBM writes are full-width. For the fp8 path the
 // same pass also writes the tile's E4M3 copy and scale byte from LDS (the
-// quantizer's rule), so the bf16 tiles are not read back.
+// quantizer's rule), so the bf16 tiles are not read back. With `means` the
+// pass also writes, for the video tiles of Q and K, each channel's mean over
+// the tile's real rows (pads are zero rows in LDS and are not counted), in
+// double and in the summation order of the mean-gate pooling kernel, so the
+// pooling need not read the tiles again.
 #include "device_common.h"
 #include "fp8_layout.h"
 #include "kernels.h"
@@ -32,12 +36,13 @@ __global__ __launch_bounds__(256) void gather_kernel(Plan p, const T *__restrict
                                                      T *__restrict__ qt, T *__restrict__ kt,
                                                      T *__restrict__ vt, uint8_t *q8,
                                                      uint8_t *k8, uint8_t *v8,
-                                                     uint8_t *scales) {
+                                                     uint8_t *scales, double *means) {
   constexpr int EPC = 16 / sizeof(T);    // elements per 16-byte chunk
   constexpr int CPR = D / EPC;           // chunks per row
   constexpr int LD = D + EPC;            // padded LDS row (keeps 16 B alignment)
   __shared__ __attribute__((aligned(16))) T tile_lds[kTile * LD];
   __shared__ float red[4];
+  __shared__ int n_real;
 
   const int tile = blockIdx.x;
   const int bh = blockIdx.y;
@@ -51,6 +56,11 @@ __global__ __launch_bounds__(256) void gather_kernel(Plan p, const T *__restrict
 
   const bool fp8 = sizeof(T) == 2 && q8 != nullptr;      // uniform over the launch
   const int32_t *map = s2t + ((int64_t)s * p.max_tiles + tile) * kTile;
+  const bool take_mean = means != nullptr && which < 2 && tile >= p.n_prefix_tiles;
+  if (take_mean && threadIdx.x < kTile) {
+    const uint64_t real = __ballot(map[threadIdx.x] >= 0);
+    if (threadIdx.x == 0) n_real = __popcll(real);
+  }
   const T *src_bh = src + (int64_t)bh * p.N * D;
   float amax = 0.f;
   for (int i = threadIdx.x; i < kTile * CPR; i += blockDim.x) {
@@ -67,6 +77,23 @@ __global__ __launch_bounds__(256) void gather_kernel(Plan p, const T *__restrict
     }
   }
   __syncthreads();
+
+  if (take_mean) {
+    // Per channel: slot pairs (r, r + 32) first, then the 32 pairs in order,
+    // as the pooling kernel adds them.
+    double *mrow = means + (((int64_t)which * p.B * p.H + bh) * p.max_vt +
+                            (tile - p.n_prefix_tiles)) * D;
+    for (int c = threadIdx.x; c < D; c += blockDim.x) {
+      double sum = 0.0;
+      for (int r = 0; r < 32; ++r) {
+        double pair = 0.0;
+        pair += (double)to_float<T>(tile_lds[r * LD + c]);
+        pair += (double)to_float<T>(tile_lds[(r + 32) * LD + c]);
+        sum += pair;
+      }
+      mrow[c] = sum / (double)n_real;
+    }
+  }
 
   T *out = dst + ((int64_t)bh * p.max_tiles + tile) * (kTile * D);
   const bool col = which == 2;
@@ -109,11 +136,12 @@ __global__ __launch_bounds__(256) void gather_kernel(Plan p, const T *__restrict
 template <typename T, int D>
 hipError_t gather_t(const Plan &p, const void *q, const void *k, const void *v,
                     const int32_t *s2t, void *qt, void *kt, void *vt, uint8_t *q8,
-                    uint8_t *k8, uint8_t *v8, uint8_t *scales, hipStream_t st) {
+                    uint8_t *k8, uint8_t *v8, uint8_t *scales, double *means,
+                    hipStream_t st) {
   dim3 grid(p.max_tiles, p.B * p.H, 3);
   hipLaunchKernelGGL((gather_kernel<T, D>), grid, dim3(256), 0, st, p,
                      (const T *)q, (const T *)k, (const T *)v, s2t, (T *)qt, (T *)kt,
-                     (T *)vt, q8, k8, v8, scales);
+                     (T *)vt, q8, k8, v8, scales, means);
   return hipGetLastError();
 }
 
@@ -129,17 +157,18 @@ hipError_t launch_build_map(const Plan &p, int32_t *s2t, hipStream_t stream) {
 
 hipError_t launch_gather(const Plan &p, const void *q, const void *k, const void *v,
                          const int32_t *s2t, void *qt, void *kt, void *vt, uint8_t *q8,
-                         uint8_t *k8, uint8_t *v8, uint8_t *scales, hipStream_t stream) {
+                         uint8_t *k8, uint8_t *v8, uint8_t *scales, hipStream_t stream,
+                         double *means) {
   if (p.dtype == VSA_BF16) {
     if (p.d == 128)
       return vsa::gather_t<bf16_bits, 128>(p, q, k, v, s2t, qt, kt, vt, q8, k8, v8, scales,
-                                           stream);
+                                           means, stream);
     return vsa::gather_t<bf16_bits, 64>(p, q, k, v, s2t, qt, kt, vt, q8, k8, v8, scales,
-                                        stream);
+                                        means, stream);
   }
   if (p.d == 128)
     return vsa::gather_t<float, 128>(p, q, k, v, s2t, qt, kt, vt, nullptr, nullptr, nullptr,
-                                     nullptr, stream);
+                                     nullptr, means, stream);
   return vsa::gather_t<float, 64>(p, q, k, v, s2t, qt, kt, vt, nullptr, nullptr, nullptr,
-                                  nullptr, stream);
+                                  nullptr, means, stream);
 }

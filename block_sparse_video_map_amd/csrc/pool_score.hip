@@ -61,6 +61,33 @@ __device__ inline void load8_f32<float>(const float *__restrict__ src, float (&v
   }
 }
 
+// Gate product of up to 16 mean rows on the f64 MFMA: mean is [16][D + 1]
+// in LDS (rows past nt zero), w the head's D x D gate, dst the first output
+// row (D doubles apart). Wave w owns 16-column blocks w, w + 4, ... A: lane l
+// holds mean[l%16][k0 + l/16]; B: gate[k0 + l/16][col0 + l%16]; D element e:
+// row 4e + l/16, column l%16.
+template <int D>
+__device__ inline void gate_rows(const double *mean, const float *__restrict__ w, double *dst,
+                                 int nt) {
+  constexpr int LM = D + 1;
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int l16 = lane % 16, g4 = lane / 16;
+  for (int cb = wave; cb < D / 16; cb += 4) {
+    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 8
+    for (int k0 = 0; k0 < D; k0 += 4) {
+      const double a = mean[l16 * LM + k0 + g4];
+      const double b = (double)w[(k0 + g4) * D + cb * 16 + l16];
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 4 * e + g4;
+      if (row < nt) dst[(int64_t)row * D + cb * 16 + l16] = acc[e];
+    }
+  }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void pool_mean_gate_kernel(
     Plan p, PoolJob job, const int32_t *__restrict__ s2t, double *__restrict__ pooled) {
@@ -128,24 +155,32 @@ __global__ __launch_bounds__(256) void pool_mean_gate_kernel(
     if (t < D) mean[tt * LM + t] = 0.0;        // rows past the last tile
   __syncthreads();
 
-  // Gate product on the f64 MFMA. A: lane l holds mean[l%16][k0 + l/16];
-  // B: gate[k0 + l/16][col0 + l%16]; D element e: row 4e + l/16, column l%16.
-  const int l16 = lane % 16, g4 = lane / 16;
-  double *dst = pooled + (((int64_t)which * nbh + bh - job.bh0) * job.rows + vt0) * D;
-  for (int cb = wave; cb < D / 16; cb += 4) {
-    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll 8
-    for (int k0 = 0; k0 < D; k0 += 4) {
-      const double a = mean[l16 * LM + k0 + g4];
-      const double b = (double)w[(k0 + g4) * D + cb * 16 + l16];
-      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc, 0, 0, 0);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 4 * e + g4;
-      if (row < nt) dst[(int64_t)row * D + cb * 16 + l16] = acc[e];
-    }
+  gate_rows<D>(mean, w, pooled + (((int64_t)which * nbh + bh - job.bh0) * job.rows + vt0) * D,
+               nt);
+}
+
+// Mean gate without the tiles: the gather pass left each video tile's means
+// at the tile's own row of `pooled`; a workgroup takes 16 rows of one
+// (batch*head, Q|K), reads them into LDS and overwrites them with their gate
+// product (the same gate_rows as the pooling kernel, so the same values).
+template <int D>
+__global__ __launch_bounds__(256) void gate_means_kernel(Plan p, const float *wq,
+                                                         const float *wk, double *pooled) {
+  constexpr int LM = D + 1;
+  __shared__ double mean[kPoolTiles * LM];
+  const int bh = blockIdx.y, which = blockIdx.z;
+  const int h = bh % p.H, s = h % p.n_shapes;
+  const int n = p.n_vt[s];
+  const int vt0 = blockIdx.x * kPoolTiles;
+  if (vt0 >= n) return;
+  const int nt = min(kPoolTiles, n - vt0);
+  double *rows = pooled + (((int64_t)which * p.B * p.H + bh) * p.max_vt + vt0) * D;
+  for (int x = threadIdx.x; x < kPoolTiles * D; x += blockDim.x) {
+    const int tt = x / D, c = x % D;
+    mean[tt * LM + c] = tt < nt ? rows[(int64_t)tt * D + c] : 0.0;
   }
+  __syncthreads();
+  gate_rows<D>(mean, (which == 0 ? wq : wk) + (int64_t)h * D * D, rows, nt);
 }
 
 // Veda TripPool: project every real token (d -> R), then the statistics the
@@ -404,6 +439,18 @@ hipError_t launch_pool(const Plan &p, int mode, int proj_dim, const PoolJob &job
   if (p.d == 128)
     return vsa::pool_t<float, 128>(p, mode, proj_dim, job, nsrc, s2t, pooled, stream);
   return vsa::pool_t<float, 64>(p, mode, proj_dim, job, nsrc, s2t, pooled, stream);
+}
+
+hipError_t launch_gate_means(const Plan &p, const float *wq, const float *wk, double *pooled,
+                             hipStream_t stream) {
+  dim3 grid((p.max_vt + vsa::kPoolTiles - 1) / vsa::kPoolTiles, p.B * p.H, 2);
+  if (p.d == 128)
+    hipLaunchKernelGGL(vsa::gate_means_kernel<128>, grid, dim3(256), 0, stream, p, wq, wk,
+                       pooled);
+  else
+    hipLaunchKernelGGL(vsa::gate_means_kernel<64>, grid, dim3(256), 0, stream, p, wq, wk,
+                       pooled);
+  return hipGetLastError();
 }
 
 hipError_t launch_scores(const Plan &p, int r, const ScoreJob &job, hipStream_t stream) {

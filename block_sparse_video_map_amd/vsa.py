@@ -32,7 +32,7 @@ VSA_FUSED_MAX_R = 192                    # vsa_tile_select: descriptor width (do
 # Names declared in include/vsa.h.
 EXPORTS = ("vsa_query_sizes", "vsa_pooled_bytes", "vsa_map_tiles", "vsa_tile_scores",
            "vsa_tile_scores_noalloc",
-           "vsa_select_topk", "vsa_tile_select", "vsa_sparse_attn_fwd", "vsa_kept_stats",
+           "vsa_select_topk", "vsa_tile_select", "vsa_map_tiles_scores", "vsa_sparse_attn_fwd", "vsa_kept_stats",
            "vsa_count_flops", "vsa_ref_sizes", "vsa_ref_pooled_bytes", "vsa_ref_scores",
            "vsa_ref_select", "vsa_sparse_attn_fwd_ref", "vsa_kept_stats_ref",
            "vsa_count_flops_ref", "vsa_teacher_map", "vsa_quantize_fp8", "vsa_map_tiles_fp8",
@@ -96,6 +96,7 @@ def lib() -> ctypes.CDLL:
             "vsa_tile_scores_noalloc": [P, i32, i32, vp, vp, vp, vp, vp, vp, vp],
             "vsa_select_topk": [P, vp, f64, vp, vp],
             "vsa_tile_select": [P, i32, i32, vp, vp, vp, vp, vp, f64, vp, vp, vp],
+            "vsa_map_tiles_scores": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "vsa_sparse_attn_fwd": [P, vp, vp, vp, vp, vp, f64, f32, vp, vp, vp],
             "vsa_kept_stats": [P, f64, ctypes.POINTER(i64), ctypes.POINTER(f64)],
             "vsa_count_flops": [P, f64, vp, vp, ctypes.POINTER(f64)],
@@ -276,6 +277,30 @@ def vsa_tile_scores(prob: Problem, mode: int, proj_dim: int, qt, kt, slot_to_tok
     _check("vsa_tile_scores", lib().vsa_tile_scores(
         prob.ref, int(mode), int(proj_dim), _ptr(qt), _ptr(kt), _ptr(slot_to_token), _ptr(wq),
         _ptr(wk), _ptr(pooled_ws), _ptr(scores), _stream(stream)))
+
+
+def vsa_map_tiles_scores(prob: Problem, q, k, v, slot_to_token, qt, kt, vt, wq, wk, pooled_ws,
+                         scores, stream=None):
+    """vsa_map_tiles + vsa_tile_scores (mean gate), the tile means taken in the gather."""
+    import torch
+    sz = vsa_query_sizes(prob, 0.0)
+    et = _elem_dtype(prob)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t is not None:
+            _need(t, sz.out_elems, et, name)
+    for name, t in (("qt", qt), ("kt", kt), ("vt", vt)):
+        if t is not None:
+            _need(t, sz.tiled_elems, et, name)
+    _need(slot_to_token, sz.map_elems, torch.int32, "slot_to_token")
+    _need(scores, sz.score_elems, torch.float32, "scores")
+    _need(wq, 1, torch.float32, "wq")
+    _need(wk, 1, torch.float32, "wk")
+    if pooled_ws.numel() * pooled_ws.element_size() < vsa_pooled_bytes(
+            prob, VSA_SCORE_MEAN_GATE, prob.d):
+        raise ValueError("pooled_ws too small")
+    _check("vsa_map_tiles_scores", lib().vsa_map_tiles_scores(
+        prob.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(slot_to_token), _ptr(qt), _ptr(kt), _ptr(vt),
+        _ptr(wq), _ptr(wk), _ptr(pooled_ws), _ptr(scores), _stream(stream)))
 
 
 def vsa_tile_scores_noalloc(prob: Problem, mode: int, proj_dim: int, qt, kt, slot_to_token, wq,
@@ -553,6 +578,10 @@ class Layer:
         if fused and not fused_select_supported(prob, mode, proj_dim, sparsity):
             raise ValueError("vsa_tile_select does not take this problem")
         self.fused = bool(fused)
+        # Mean gate: forward() gathers and pools in one pass (vsa_map_tiles_scores),
+        # which writes exactly what vsa_map_tiles + vsa_tile_scores write.
+        self.gather_pool = (mode == VSA_SCORE_MEAN_GATE and not fp8 and sparsity != 0.0
+                            and not self.fused)
         self.sizes = sz = vsa_query_sizes(prob, sparsity)
         et = _elem_dtype(prob)
         dev = torch.device(device)
@@ -594,6 +623,16 @@ class Layer:
     def quantize(self, stream=None):
         vsa_quantize_fp8(self.prob, self.qt, self.kt, self.vt, self.q8, self.k8, self.v8,
                          self.fp8_scales, stream)
+
+    def map_tiles_scores(self, q, k, v, wq, wk, stream=None):
+        """map_tiles + tile_scores (mean gate) with the tile means taken in the
+        gather pass."""
+        vsa_map_tiles_scores(self.prob, q, k, v, self.slot_to_token, self.qt, self.kt, self.vt,
+                             wq, wk, self.pooled, self.scores, stream)
+        if self.budget is not None:
+            vsa_ref_scores(self.prob, self.mode, self.proj_dim, self.kt, self.slot_to_token, wq,
+                           wk, self.budget, self.pooled, self.ref_pooled, self.ref_scores,
+                           stream)
 
     def tile_scores(self, wq, wk, stream=None):
         vsa_tile_scores(self.prob, self.mode, self.proj_dim, self.qt, self.kt,
@@ -644,17 +683,21 @@ class Layer:
 
     def forward(self, q, k, v, wq, wk, softmax_scale: float = 0.0, stream=None):
         """One whole layer: map+gather, scores, top-k, attention (fp8: the
-        gather also writes the E4M3 tiles). Scores and top-k are one call
+        gather also writes the E4M3 tiles). Gather and mean-gate pooling are
+        one call when self.gather_pool; scores and top-k are one call
         (vsa_tile_select) when self.fused."""
         if self.fp8:
             self.map_tiles_fp8(q, k, v, stream)
+        elif self.gather_pool:
+            self.map_tiles_scores(q, k, v, wq, wk, stream)
         else:
             self.map_tiles(q, k, v, stream)
         if self.sparsity != 0.0:
             if self.fused:
                 self.score_select(wq, wk, stream)
             else:
-                self.tile_scores(wq, wk, stream)
+                if not self.gather_pool:
+                    self.tile_scores(wq, wk, stream)
                 self.select(stream)
         self.attend(softmax_scale, stream)
         return self.out

@@ -193,6 +193,42 @@ def assert_fused_equal(run: GpuRun, sparsity=None):
     return True
 
 
+def assert_gather_pool_equal(run: GpuRun):
+    """vsa_map_tiles_scores (gather with the tile means, gate, scores) writes
+    bit for bit what vsa_map_tiles + vsa_tile_scores wrote into the run's
+    layer: tile map, tiled Q/K/V, descriptors and scores. Mean gate only;
+    returns False for other scorers."""
+    import torch
+    from block_sparse_video_map_amd import vsa
+    w, L = run.w, run.layer
+    if L.mode != vsa.VSA_SCORE_MEAN_GATE:
+        return False
+    s2t = torch.full_like(L.slot_to_token, -7)
+    qt, kt, vt = (torch.zeros_like(L.qt) for _ in range(3))
+    pooled = torch.full_like(L.pooled, float("nan"))
+    scores = torch.full_like(L.scores, float("nan"))
+    vsa.vsa_map_tiles_scores(run.prob, run.q, run.k, run.v, s2t, qt, kt, vt, run.wq, run.wk,
+                             pooled, scores)
+    torch.cuda.synchronize()
+    sz = L.sizes
+    assert torch.equal(s2t, L.slot_to_token)
+    per_head = sz.max_tiles * 64 * w.d
+    nv, BH = sz.max_video_tiles, w.B * w.H
+    sc_a, sc_b = L.scores.view(BH, nv, nv), scores.view(BH, nv, nv)
+    pd_a = L.pooled[: 2 * BH * nv * w.d].view(2, BH, nv, w.d)
+    pd_b = pooled[: 2 * BH * nv * w.d].view(2, BH, nv, w.d)
+    for bh in range(BH):
+        si = (bh % w.H) % len(w.tile_shapes)
+        nt, n = sz.n_tiles[si], sz.n_video_tiles[si]
+        for a, b in ((L.qt, qt), (L.kt, kt), (L.vt, vt)):
+            seg = slice(bh * per_head, bh * per_head + nt * 64 * w.d)
+            assert torch.equal(a[seg], b[seg]), bh
+        assert torch.equal(pd_a[:, bh, :n], pd_b[:, bh, :n]), bh
+        assert torch.equal(sc_a[bh, :n, :n], sc_b[bh, :n, :n]), bh
+    log(f"[gather-pool] {w.name}: one-pass gather and pooling equal the two calls")
+    return True
+
+
 def tensor_f32(t) -> np.ndarray:
     import torch
     if t.dtype == torch.bfloat16:

@@ -490,3 +490,23 @@ def test_fused_select_support_rule():
     too = vsa.Problem(1, 1, 128, (1, 1, 64 * (n + 1)), (), ((1, 1, 64),), "bf16")
     assert vsa.fused_select_supported(ok, vsa.VSA_SCORE_MEAN_GATE, 128, 0.9)
     assert not vsa.fused_select_supported(too, vsa.VSA_SCORE_MEAN_GATE, 128, 0.9)
+
+
+def test_map_tiles_scores_rejects_before_launch():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host-only check; skipped where a GPU is visible")
+    L = vsa.lib()
+    fake, odd = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x10008)
+    p = _problem(WORKLOADS["1"])
+    f = lambda **kw: L.vsa_map_tiles_scores(
+        p.ref, kw.get("q", fake), kw.get("k", fake), kw.get("v", fake), kw.get("s2t", fake),
+        kw.get("qt", fake), kw.get("kt", fake), kw.get("vt", fake), kw.get("wq", fake), None,
+        kw.get("ws", fake), kw.get("sc", fake), None)
+    odd4 = ctypes.c_void_p(0x10004)         # workspace of doubles: 8-byte alignment
+    for kw in (dict(q=None), dict(k=None), dict(s2t=None), dict(qt=None), dict(wq=None),
+               dict(ws=None), dict(sc=None), dict(vt=None), dict(q=odd), dict(ws=odd4)):
+        assert f(**kw) == vsa.VSA_ERR_INVALID_ARG, kw
+    bad = _problem(WORKLOADS["1"], d=96)
+    assert L.vsa_map_tiles_scores(bad.ref, fake, fake, fake, fake, fake, fake, fake, fake, None,
+                                  fake, fake, None) == vsa.VSA_ERR_UNSUPPORTED

@@ -96,6 +96,7 @@ def test_edge_workload_full_parity(name):
                                               oracle.gather(x, tm))
     _full_check(w, run)
     gs.assert_fused_equal(run)
+    gs.assert_gather_pool_equal(run)
 
 
 def test_dense_path_equals_dense_attention():
@@ -141,6 +142,7 @@ def test_exact_ties_go_to_lower_index():
             assert not (3 in row or 6 in row) or 1 in row
             assert 7 not in row or 0 in row
     assert gs.assert_fused_equal(run)
+    assert gs.assert_gather_pool_equal(run)
 
 
 def test_deterministic_and_batch_independent():

@@ -131,6 +131,14 @@ def test_fused_select_equals_two_calls(run):
     assert gs.assert_fused_equal(run), "every workload is within vsa_tile_select's limits"
 
 
+def test_gather_pool_equals_two_calls(run):
+    """Mean-gate workloads: vsa_map_tiles_scores writes exactly what
+    vsa_map_tiles + vsa_tile_scores write (checked against the oracle above)."""
+    gs.log(f"[parity] one-pass gather and pooling {run.name}")
+    done = gs.assert_gather_pool_equal(run)
+    assert done == (run.w.scorer == "mean_gate")
+
+
 def _pick_tiles(tm, count, seed):
     if count is None:
         return list(range(tm.n_tiles))
