@@ -13,17 +13,6 @@
 namespace vsa {
 namespace {
 
-// Unpacks one row-layout tile of T into LDS as float [64][LD].
-template <typename T, int D, int LD>
-__device__ inline void load_tile_f32(const T *__restrict__ src, float *xs) {
-  for (int vec = threadIdx.x; vec < kTile * D / 8; vec += blockDim.x) {
-    int sl, c;
-    row_layout_decode(vec, 0, D, sl, c);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) xs[sl * LD + c + e] = to_float<T>(src[vec * 8 + e]);
-  }
-}
-
 // VSA: desc = mean over real slots, times the head's gate.
 //
 // One workgroup takes 16 video tiles of one (batch*head, Q|K). Means: every
@@ -185,24 +174,24 @@ __global__ __launch_bounds__(256) void gate_means_kernel(Plan p, const float *wq
 
 // Veda TripPool: project every real token (d -> R), then the statistics the
 // mode asks for, written in the order [Avg | Max | Min] (bits 1, 2, 4 of stats).
-// A workgroup takes kTripTiles consecutive tiles of one (batch*head, Q|K) and
-// stages the head's projection in LDS once for all of them.
-// The projection X[64 tokens x D] . P[D x R] runs on the 16x16x4 f64 MFMA:
-// wave w owns tokens 16w..16w+15 and all R columns (16-column blocks). Lane
-// l reads four consecutive channels k0 + 4*(l/16) + m of its token row and of
-// its column of P (transposed in LDS), MFMA m contracting channel m of that
-// group. Each lane then holds four tokens (rows 4e + l/16) of one column
-// (l % 16); the statistics are reduced across lanes, then across waves.
+// A workgroup of four waves takes kTripTiles consecutive tiles of one
+// (batch*head, Q|K), stages the head's projection in LDS once (transposed,
+// float) and gives each wave its own tiles: no barrier inside the tile loop.
+// The projection X[64 tokens x D] . P[D x R] runs on the 16x16x4 f64 MFMA,
+// 4 x RB blocks of 16 tokens x 16 columns per wave. Lane l reads the four
+// consecutive channels k0 + 4*(l/16) + m of its token row straight from the
+// tiled copy (8 or 16 contiguous bytes) and of its column of P; MFMA m
+// contracts channel m of each lane's group. Element e of block (rb, cb) in
+// lane l is token 16 rb + 4e + l/16, column 16 cb + l%16. The statistics
+// reduce the four elements of a lane, the four lanes of a column, then the
+// four token blocks in order.
 template <typename T, int D, int R>
 __global__ __launch_bounds__(256) void pool_trippool_kernel(
     Plan p, PoolJob job, int stats, const int32_t *__restrict__ s2t,
     double *__restrict__ pooled) {
   constexpr int LD = D + 4;                  // float rows, 16-byte aligned
   constexpr int RB = (R + 15) / 16;          // 16-column blocks
-  __shared__ __attribute__((aligned(16))) float xs[kTile * LD];
   __shared__ __attribute__((aligned(16))) float pt[RB * 16 * LD];   // P transposed
-  __shared__ double red[3][4][RB * 16];      // [stat][wave][column]
-  __shared__ int valid[kTile];
 
   const int bh = job.bh0 + blockIdx.y, which = blockIdx.z;
   const int nbh = job.nbh < 0 ? p.B * p.H : job.nbh;
@@ -219,88 +208,104 @@ __global__ __launch_bounds__(256) void pool_trippool_kernel(
     const int j = i % (RB * 16), c = i / (RB * 16);   // pt[j][c] = P[c][j], zero past R
     pt[j * LD + c] = j < R ? w[c * R + j] : 0.f;
   }
+  __syncthreads();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
   const int lane = threadIdx.x % 64, g = lane / 16, l16 = lane % 16;
+  const int width = __builtin_popcount(stats) * R;
 
-  for (int vt_i = first; vt_i < last; ++vt_i) {
+  for (int vt_i = first + wave; vt_i < last; vt_i += 4) {
     const int tile = job.tile0 + vt_i;
     const T *src = (const T *)job.src[which] + ((int64_t)bh * p.max_tiles + tile) * (kTile * D);
-    __syncthreads();                         // the previous tile's LDS reads are done
-    if (threadIdx.x < kTile)
-      valid[threadIdx.x] = s2t[((int64_t)s * p.max_tiles + tile) * kTile + threadIdx.x] >= 0;
-    load_tile_f32<T, D, LD>(src, xs);
-    __syncthreads();
+    const uint64_t valid = __ballot(s2t[((int64_t)s * p.max_tiles + tile) * kTile + lane] >= 0);
+    const int n = __popcll(valid);
 
-    f64x4 acc[RB];
+    f64x4 acc[4][RB];
 #pragma unroll
-    for (int b = 0; b < RB; ++b) acc[b] = (f64x4){0.0, 0.0, 0.0, 0.0};
-    const float *xrow = xs + (wave * 16 + l16) * LD;
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < RB; ++cb) acc[rb][cb] = (f64x4){0.0, 0.0, 0.0, 0.0};
+    // Token 16 rb + l16, channels k0 + 4g .. +3 in the row layout: slot
+    // group (16 rb + l16) / 32, channel block k0 / 16, half g / 2, offset
+    // 4 (g % 2) within the 8-channel run.
 #pragma unroll 2
     for (int k0 = 0; k0 < D; k0 += 16) {
-      const int kk = k0 + 4 * g;
-      const float4 xa = *reinterpret_cast<const float4 *>(xrow + kk);
-      const double a4[4] = {xa.x, xa.y, xa.z, xa.w};
+      double a4[4][4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const int sl = 16 * rb + l16;
+        const T *x = src + ((sl / 32) * (D / 16) + k0 / 16) * 512 + ((g / 2) * 32 + sl % 32) * 8 +
+                     4 * (g % 2);
+        if constexpr (sizeof(T) == 2) {
+          const uint2 w2 = *reinterpret_cast<const uint2 *>(x);
+          a4[rb][0] = __uint_as_float(w2.x << 16);
+          a4[rb][1] = __uint_as_float(w2.x & 0xFFFF0000u);
+          a4[rb][2] = __uint_as_float(w2.y << 16);
+          a4[rb][3] = __uint_as_float(w2.y & 0xFFFF0000u);
+        } else {
+          const float4 f4 = *reinterpret_cast<const float4 *>(x);
+          a4[rb][0] = f4.x;
+          a4[rb][1] = f4.y;
+          a4[rb][2] = f4.z;
+          a4[rb][3] = f4.w;
+        }
+      }
       double b4[RB][4];
 #pragma unroll
-      for (int b = 0; b < RB; ++b) {
-        const float4 pb = *reinterpret_cast<const float4 *>(pt + (b * 16 + l16) * LD + kk);
-        b4[b][0] = pb.x; b4[b][1] = pb.y; b4[b][2] = pb.z; b4[b][3] = pb.w;
+      for (int cb = 0; cb < RB; ++cb) {
+        const float4 pb = *reinterpret_cast<const float4 *>(pt + (cb * 16 + l16) * LD + k0 + 4 * g);
+        b4[cb][0] = pb.x;
+        b4[cb][1] = pb.y;
+        b4[cb][2] = pb.z;
+        b4[cb][3] = pb.w;
       }
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int b = 0; b < RB; ++b)
-          acc[b] = __builtin_amdgcn_mfma_f64_16x16x4f64(a4[m], b4[b][m], acc[b], 0, 0, 0);
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < RB; ++cb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(a4[rb][m], b4[cb][m], acc[rb][cb],
+                                                              0, 0, 0);
     }
 
-    // Element e of lane l: token wave*16 + 4e + l/16, column b*16 + l%16.
+    double *out0 = pooled + (((int64_t)which * nbh + bh - job.bh0) * job.rows + vt_i) * width;
 #pragma unroll
-    for (int b = 0; b < RB; ++b) {
-      double sum = 0.0, mx = -INFINITY, mn = INFINITY;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (valid[wave * 16 + 4 * e + g]) {
-          sum += acc[b][e];
-          mx = fmax(mx, acc[b][e]);
-          mn = fmin(mn, acc[b][e]);
-        }
-      }
-#pragma unroll
-      for (int d = 16; d < 64; d <<= 1) {    // the four lanes of a column
-        sum += __shfl_xor(sum, d);
-        mx = fmax(mx, __shfl_xor(mx, d));
-        mn = fmin(mn, __shfl_xor(mn, d));
-      }
-      if (g == 0) {
-        red[0][wave][b * 16 + l16] = sum;
-        red[1][wave][b * 16 + l16] = mx;
-        red[2][wave][b * 16 + l16] = mn;
-      }
-    }
-    __syncthreads();
-
-    if (threadIdx.x < R) {
-      const int j = threadIdx.x;
-      int n = 0;
-      for (int sl = 0; sl < kTile; ++sl) n += valid[sl];
+    for (int cb = 0; cb < RB; ++cb) {
       double ts = 0.0, tx = -INFINITY, tn = INFINITY;
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww) {
-        ts += red[0][ww][j];
-        tx = fmax(tx, red[1][ww][j]);
-        tn = fmin(tn, red[2][ww][j]);
+      for (int rb = 0; rb < 4; ++rb) {
+        double sum = 0.0, mx = -INFINITY, mn = INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if ((valid >> (16 * rb + 4 * e + g)) & 1ull) {
+            sum += acc[rb][cb][e];
+            mx = fmax(mx, acc[rb][cb][e]);
+            mn = fmin(mn, acc[rb][cb][e]);
+          }
+        }
+#pragma unroll
+        for (int d = 16; d < 64; d <<= 1) {  // the four lanes of a column
+          sum += __shfl_xor(sum, d);
+          mx = fmax(mx, __shfl_xor(mx, d));
+          mn = fmin(mn, __shfl_xor(mn, d));
+        }
+        ts += sum;
+        tx = fmax(tx, mx);
+        tn = fmin(tn, mn);
       }
-      const int width = __builtin_popcount(stats) * R;
-      double *out = pooled + (((int64_t)which * nbh + bh - job.bh0) * job.rows + vt_i) * width + j;
-      if (stats & 1) {
-        *out = ts / (double)n;
-        out += R;
+      const int j = cb * 16 + l16;
+      if (g == 0 && j < R) {
+        double *out = out0 + j;
+        if (stats & 1) {
+          *out = ts / (double)n;
+          out += R;
+        }
+        if (stats & 2) {
+          *out = tx;
+          out += R;
+        }
+        if (stats & 4) *out = tn;
       }
-      if (stats & 2) {
-        *out = tx;
-        out += R;
-      }
-      if (stats & 4) *out = tn;
     }
   }
 }
