@@ -1,6 +1,6 @@
 // Step 3: top-k video key tiles per video query tile.
 //
-// Rows of up to 2048 keys: one wave per score row, four rows per workgroup;
+// Rows of up to 4096 keys: one wave per score row, four rows per workgroup;
 // the waves never wait for one another (longer rows: one workgroup per row,
 // below). Scores become order-preserving 32-bit keys (larger key =
 // larger score, -0.0 folded into +0.0) held in registers; lane l holds
@@ -56,10 +56,14 @@ __global__ __launch_bounds__(kSelThreads) void select_wave_kernel(Plan p, Select
   // above it, so those keys never enter a histogram or the kept set.
   uint32_t key[E];
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  // Loads from a clamped index, unconditionally: a load under a per-element
+  // branch is waited for before the next one is issued.
+  float x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = row[min(e * 64 + lane, n - 1)];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int j = e * 64 + lane;
-    key[e] = j < n ? order_key(row[j]) : 0u;
+    key[e] = e * 64 + lane < n ? order_key(x[e]) : 0u;
     lo = min(lo, key[e] ? key[e] : 0xFFFFFFFFu);
     hi = max(hi, key[e]);
   }
@@ -150,10 +154,10 @@ __device__ inline int block_exclusive_scan(int v, int *wave_tot, int &total) {
   return base + incl - v;
 }
 
-// Rows longer than 2048 keys: one workgroup of four waves per row, each
+// Rows longer than 4096 keys: one workgroup of four waves per row, each
 // thread owning a contiguous run of E indices; the same search, with the
-// histogram and the scans shared by the workgroup (for long rows this beats
-// one wave per row, whose 64 keys per lane serialise in the histogram).
+// histogram and the scans shared by the workgroup (one wave would hold 128
+// keys per lane).
 // E = keys per thread (n <= E * kSelThreads).
 template <int E>
 __global__ __launch_bounds__(kSelThreads) void select_block_kernel(Plan p, SelectJob job) {
@@ -171,8 +175,11 @@ __global__ __launch_bounds__(kSelThreads) void select_block_kernel(Plan p, Selec
 
   const float *row = job.scores + (int64_t)bh * job.in_bh + (int64_t)i * job.in_row;
   uint32_t key[E];
+  float x[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) key[e] = (j0 + e < n) ? order_key(row[j0 + e]) : 0u;
+  for (int e = 0; e < E; ++e) x[e] = row[min(j0 + e, n - 1)];   // unconditional: see above
+#pragma unroll
+  for (int e = 0; e < E; ++e) key[e] = (j0 + e < n) ? order_key(x[e]) : 0u;
 
   // The row's key range.
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
@@ -268,14 +275,16 @@ __global__ __launch_bounds__(kSelThreads) void select_block_kernel(Plan p, Selec
 
 hipError_t launch_select(const Plan &p, const SelectJob &job, hipStream_t stream) {
   dim3 block(vsa::kSelThreads);
-  if (job.max_cols <= 2048) {
+  if (job.max_cols <= 4096) {
     dim3 grid((p.max_vt + vsa::kSelWaves - 1) / vsa::kSelWaves, p.B * p.H);
     if (job.max_cols <= 512)
       hipLaunchKernelGGL(vsa::select_wave_kernel<8>, grid, block, 0, stream, p, job);
     else if (job.max_cols <= 1024)
       hipLaunchKernelGGL(vsa::select_wave_kernel<16>, grid, block, 0, stream, p, job);
-    else
+    else if (job.max_cols <= 2048)
       hipLaunchKernelGGL(vsa::select_wave_kernel<32>, grid, block, 0, stream, p, job);
+    else
+      hipLaunchKernelGGL(vsa::select_wave_kernel<64>, grid, block, 0, stream, p, job);
   } else {
     if (job.max_cols > 8192) return hipErrorInvalidValue;
     dim3 grid(p.max_vt, p.B * p.H);

@@ -19,6 +19,10 @@ subset of heads can be regenerated on its own):
   all float32.
 * bf16 workloads round Q, K and V to bfloat16 (round to nearest even) once,
   here; both sides read exactly those values.
+* Score rows for the select step alone (row lengths no workload reaches):
+  even rows N(0, 1) float32; odd rows drawn from the 81 levels j/8,
+  j = -40..40, so that exact ties are common, with -0.0 in place of +0.0 in
+  every other tied zero.
 """
 
 from __future__ import annotations
@@ -31,7 +35,7 @@ import numpy as np
 from .configs import Workload
 
 _TAG = {"q": 1, "k": 2, "v": 3, "qk_wave": 4, "v_wave": 5,
-        "gate": 6, "proj_q": 7, "proj_k": 8}
+        "gate": 6, "proj_q": 7, "proj_k": 8, "score_rows": 9}
 
 
 def _rng(seed: int, tag: str, b: int, h: int) -> np.random.Generator:
@@ -137,3 +141,14 @@ def make_weights(w: Workload) -> dict:
     pk = np.stack([_rng(w.seed, "proj_k", 0, h).standard_normal(
         (w.d, w.proj_dim)) * std for h in range(w.H)]).astype(np.float32)
     return {"proj_q": pq, "proj_k": pk}
+
+
+def score_rows(seed: int, n_rows: int, n: int) -> np.ndarray:
+    """float32 [n_rows, n] synthetic tile scores (see the recipe above)."""
+    g = _rng(seed, "score_rows", 0, 0)
+    out = g.standard_normal((n_rows, n), dtype=np.float32)
+    levels = g.integers(-40, 41, size=(n_rows // 2, n)).astype(np.float32) / np.float32(8.0)
+    zero = levels == 0
+    levels[zero & (np.arange(n)[None, :] % 2 == 1)] = np.float32(-0.0)
+    out[1::2] = levels
+    return out
