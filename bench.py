@@ -257,7 +257,8 @@ class Case:
         r = w.d if w.scorer == "mean_gate" else nstat * w.proj_dim
         out = {"map_gather": 3 * es * w.B * w.H * w.N * w.d + 3 * es * tiles * 64 * w.d}
         if self.sparsity != 0.0 and self.layer.gather_pool:
-            # the gather, then descriptors written, gated in place and read by the scores
+            # the gather with the pooling, descriptors written (and gated in place for
+            # the mean gate) and read by the scores
             out.pop("map_gather")
             out["map_gather_scores"] = (3 * es * w.B * w.H * w.N * w.d + 3 * es * tiles * 64 * w.d
                                         + 4 * 8 * vt * r + 4 * vt2)

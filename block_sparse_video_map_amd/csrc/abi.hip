@@ -53,42 +53,66 @@ VSA_API int vsa_map_tiles(const vsa_problem *prob, const void *q, const void *k,
                                   nullptr, nullptr, s));
 }
 
-VSA_API int vsa_map_tiles_scores(const vsa_problem *prob, const void *q, const void *k,
-                                 const void *v, int32_t *slot_to_token, void *qt, void *kt,
-                                 void *vt, const float *wq, const float *wk, void *pooled_ws,
+VSA_API int vsa_map_tiles_scores(const vsa_problem *prob, int32_t mode, int32_t proj_dim,
+                                 const void *q, const void *k, const void *v,
+                                 int32_t *slot_to_token, void *qt, void *kt, void *vt,
+                                 const float *wq, const float *wk, void *pooled_ws,
                                  float *scores, void *stream) {
   Plan p;
   int st = make_plan_geometry(prob, &p);
   if (st != VSA_OK) return st;
   int64_t bytes = 0;
-  st = vsa_pooled_bytes(prob, VSA_SCORE_MEAN_GATE, p.d, &bytes);
+  st = vsa_pooled_bytes(prob, mode, proj_dim, &bytes);
   if (st != VSA_OK) return st;
   if (!slot_to_token || !q || !k || !qt || !kt || !wq || !pooled_ws || !scores)
     return VSA_ERR_INVALID_ARG;
+  if (mode != VSA_SCORE_MEAN_GATE && !wk) return VSA_ERR_INVALID_ARG;
   if ((v == nullptr) != (vt == nullptr)) return VSA_ERR_INVALID_ARG;
   const void *in[3] = {q, k, v};
   void *outp[3] = {qt, kt, vt};
   for (int i = 0; i < 3; ++i)
     if (!aligned16(in[i]) || !aligned16(outp[i])) return VSA_ERR_INVALID_ARG;
   if ((uintptr_t)pooled_ws & 7u) return VSA_ERR_INVALID_ARG;
+  int r = 0;
+  descriptor_width(mode, proj_dim, p.d, &r);         // validated by vsa_pooled_bytes
   hipStream_t s = (hipStream_t)stream;
   double *pooled = (double *)pooled_ws;
   if (launch_build_map(p, slot_to_token, s) != hipSuccess) return VSA_ERR_HIP;
-  if (launch_gather(p, q, k, v, slot_to_token, qt, kt, vt, nullptr, nullptr, nullptr, nullptr,
-                    s, pooled) != hipSuccess)
-    return VSA_ERR_HIP;
-  if (launch_gate_means(p, wq, wk ? wk : wq, pooled, s) != hipSuccess) return VSA_ERR_HIP;
+  if (mode == VSA_SCORE_MEAN_GATE) {
+    if (launch_gather(p, q, k, v, slot_to_token, qt, kt, vt, nullptr, nullptr, nullptr, nullptr,
+                      s, pooled) != hipSuccess)
+      return VSA_ERR_HIP;
+    if (launch_gate_means(p, wq, wk ? wk : wq, pooled, s) != hipSuccess) return VSA_ERR_HIP;
+  } else {
+    // TripPool: the plain gather, then the pooling kernel (projecting inside
+    // the gather measured slower: the workgroup's memory phase and its f64
+    // phase no longer overlap with other workgroups' at the gather's
+    // occupancy).
+    if (launch_gather(p, q, k, v, slot_to_token, qt, kt, vt, nullptr, nullptr, nullptr, nullptr,
+                      s) != hipSuccess)
+      return VSA_ERR_HIP;
+    PoolJob job;
+    job.tile0 = p.n_prefix_tiles;
+    job.ntiles = -1;
+    job.rows = p.max_vt;
+    job.src[0] = qt;
+    job.src[1] = kt;
+    job.w[0] = wq;
+    job.w[1] = wk;
+    if (launch_pool(p, mode, proj_dim, job, 2, slot_to_token, pooled, s) != hipSuccess)
+      return VSA_ERR_HIP;
+  }
   const int64_t bh = (int64_t)p.B * p.H;
   ScoreJob sj;
   sj.q = pooled;
-  sj.q_bh = (int64_t)p.max_vt * p.d;
-  sj.k = pooled + bh * p.max_vt * p.d;
-  sj.k_bh = (int64_t)p.max_vt * p.d;
+  sj.q_bh = (int64_t)p.max_vt * r;
+  sj.k = pooled + bh * p.max_vt * r;
+  sj.k_bh = (int64_t)p.max_vt * r;
   sj.ncols = -1;
   sj.out = scores;
   sj.out_row = p.max_vt;
   sj.out_bh = (int64_t)p.max_vt * p.max_vt;
-  return hip_status(launch_scores(p, p.d, sj, s));
+  return hip_status(launch_scores(p, r, sj, s));
 }
 
 VSA_API int vsa_map_tiles_fp8(const vsa_problem *prob, const void *q, const void *k,

@@ -96,7 +96,7 @@ def lib() -> ctypes.CDLL:
             "vsa_tile_scores_noalloc": [P, i32, i32, vp, vp, vp, vp, vp, vp, vp],
             "vsa_select_topk": [P, vp, f64, vp, vp],
             "vsa_tile_select": [P, i32, i32, vp, vp, vp, vp, vp, f64, vp, vp, vp],
-            "vsa_map_tiles_scores": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+            "vsa_map_tiles_scores": [P, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "vsa_sparse_attn_fwd": [P, vp, vp, vp, vp, vp, f64, f32, vp, vp, vp],
             "vsa_kept_stats": [P, f64, ctypes.POINTER(i64), ctypes.POINTER(f64)],
             "vsa_count_flops": [P, f64, vp, vp, ctypes.POINTER(f64)],
@@ -279,9 +279,10 @@ def vsa_tile_scores(prob: Problem, mode: int, proj_dim: int, qt, kt, slot_to_tok
         _ptr(wk), _ptr(pooled_ws), _ptr(scores), _stream(stream)))
 
 
-def vsa_map_tiles_scores(prob: Problem, q, k, v, slot_to_token, qt, kt, vt, wq, wk, pooled_ws,
-                         scores, stream=None):
-    """vsa_map_tiles + vsa_tile_scores (mean gate), the tile means taken in the gather."""
+def vsa_map_tiles_scores(prob: Problem, mode: int, proj_dim: int, q, k, v, slot_to_token, qt, kt,
+                         vt, wq, wk, pooled_ws, scores, stream=None):
+    """vsa_map_tiles + vsa_tile_scores in one call (mean gate: the pooling done
+    in the gather pass)."""
     import torch
     sz = vsa_query_sizes(prob, 0.0)
     et = _elem_dtype(prob)
@@ -295,12 +296,12 @@ def vsa_map_tiles_scores(prob: Problem, q, k, v, slot_to_token, qt, kt, vt, wq, 
     _need(scores, sz.score_elems, torch.float32, "scores")
     _need(wq, 1, torch.float32, "wq")
     _need(wk, 1, torch.float32, "wk")
-    if pooled_ws.numel() * pooled_ws.element_size() < vsa_pooled_bytes(
-            prob, VSA_SCORE_MEAN_GATE, prob.d):
+    if pooled_ws.numel() * pooled_ws.element_size() < vsa_pooled_bytes(prob, mode, proj_dim):
         raise ValueError("pooled_ws too small")
     _check("vsa_map_tiles_scores", lib().vsa_map_tiles_scores(
-        prob.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(slot_to_token), _ptr(qt), _ptr(kt), _ptr(vt),
-        _ptr(wq), _ptr(wk), _ptr(pooled_ws), _ptr(scores), _stream(stream)))
+        prob.ref, int(mode), int(proj_dim), _ptr(q), _ptr(k), _ptr(v), _ptr(slot_to_token),
+        _ptr(qt), _ptr(kt), _ptr(vt), _ptr(wq), _ptr(wk), _ptr(pooled_ws), _ptr(scores),
+        _stream(stream)))
 
 
 def vsa_tile_scores_noalloc(prob: Problem, mode: int, proj_dim: int, qt, kt, slot_to_token, wq,
@@ -625,10 +626,9 @@ class Layer:
                          self.fp8_scales, stream)
 
     def map_tiles_scores(self, q, k, v, wq, wk, stream=None):
-        """map_tiles + tile_scores (mean gate) with the tile means taken in the
-        gather pass."""
-        vsa_map_tiles_scores(self.prob, q, k, v, self.slot_to_token, self.qt, self.kt, self.vt,
-                             wq, wk, self.pooled, self.scores, stream)
+        """map_tiles + tile_scores with the pooling done in the gather pass."""
+        vsa_map_tiles_scores(self.prob, self.mode, self.proj_dim, q, k, v, self.slot_to_token,
+                             self.qt, self.kt, self.vt, wq, wk, self.pooled, self.scores, stream)
         if self.budget is not None:
             vsa_ref_scores(self.prob, self.mode, self.proj_dim, self.kt, self.slot_to_token, wq,
                            wk, self.budget, self.pooled, self.ref_pooled, self.ref_scores,
@@ -683,8 +683,8 @@ class Layer:
 
     def forward(self, q, k, v, wq, wk, softmax_scale: float = 0.0, stream=None):
         """One whole layer: map+gather, scores, top-k, attention (fp8: the
-        gather also writes the E4M3 tiles). Gather and mean-gate pooling are
-        one call when self.gather_pool; scores and top-k are one call
+        gather also writes the E4M3 tiles). Gather and pooling are one call
+        when self.gather_pool; scores and top-k are one call
         (vsa_tile_select) when self.fused."""
         if self.fp8:
             self.map_tiles_fp8(q, k, v, stream)

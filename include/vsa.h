@@ -196,23 +196,27 @@ VSA_API int vsa_tile_scores(const vsa_problem *prob, int32_t mode,
                             void *stream);
 
 /*
- * vsa_map_tiles_scores - vsa_map_tiles followed by vsa_tile_scores in mode
- * VSA_SCORE_MEAN_GATE (proj_dim = d), with the pooling's tile means taken in
- * the gather pass, so the tiled Q and K are not read back (the pages' engine
- * gathers whole tiles in one pass: "BSAI-ComfyUI-VedaSparse" README,
- * Implementation section). Writes exactly what the two calls write:
- * slot_to_token, qt, kt, vt, the workspace's descriptors and the scores,
- * bit for bit.
+ * vsa_map_tiles_scores - vsa_map_tiles followed by vsa_tile_scores in one call;
+ * for the mean gate the pooling is done in the gather pass, so the tiled Q and
+ * K are not read back (the pages' engine gathers whole tiles in one pass: "BSAI-ComfyUI-VedaSparse"
+ * README, Implementation section). Mean gate: the gather takes each video
+ * tile's channel means, then the gate product follows. TripPool modes: the
+ * gather, then the pooling kernel, as the two calls run them (the projection
+ * needs every token's row, which the pooling reads once). Writes exactly what
+ * the two calls write: slot_to_token, qt, kt, vt, the workspace's
+ * descriptors and the scores, bit for bit.
  *
- * Arguments as the two calls: q, k (and v, or v = vt = NULL) device inputs;
- * wq (and wk, or NULL for wq) the float [H][d][d] gates; pooled_ws of
- * vsa_pooled_bytes(prob, VSA_SCORE_MEAN_GATE, d) bytes.
+ * Arguments as the two calls: mode and proj_dim as vsa_tile_scores; q, k
+ * (and v, or v = vt = NULL) device inputs; wq, wk as vsa_tile_scores
+ * (mean gate: wk may be NULL for wq); pooled_ws of
+ * vsa_pooled_bytes(prob, mode, proj_dim) bytes.
  */
-VSA_API int vsa_map_tiles_scores(const vsa_problem *prob, const void *q,
-                                 const void *k, const void *v,
-                                 int32_t *slot_to_token, void *qt, void *kt,
-                                 void *vt, const float *wq, const float *wk,
-                                 void *pooled_ws, float *scores, void *stream);
+VSA_API int vsa_map_tiles_scores(const vsa_problem *prob, int32_t mode,
+                                 int32_t proj_dim, const void *q, const void *k,
+                                 const void *v, int32_t *slot_to_token, void *qt,
+                                 void *kt, void *vt, const float *wq,
+                                 const float *wk, void *pooled_ws, float *scores,
+                                 void *stream);
 
 /*
  * vsa_tile_scores_noalloc - vsa_tile_scores for callers that cannot allocate

@@ -194,29 +194,27 @@ def assert_fused_equal(run: GpuRun, sparsity=None):
 
 
 def assert_gather_pool_equal(run: GpuRun):
-    """vsa_map_tiles_scores (gather with the tile means, gate, scores) writes
-    bit for bit what vsa_map_tiles + vsa_tile_scores wrote into the run's
-    layer: tile map, tiled Q/K/V, descriptors and scores. Mean gate only;
-    returns False for other scorers."""
+    """vsa_map_tiles_scores (the pooling done in the gather pass, then the
+    scores) writes bit for bit what vsa_map_tiles + vsa_tile_scores wrote into
+    the run's layer: tile map, tiled Q/K/V, descriptors and scores."""
     import torch
     from block_sparse_video_map_amd import vsa
     w, L = run.w, run.layer
-    if L.mode != vsa.VSA_SCORE_MEAN_GATE:
-        return False
     s2t = torch.full_like(L.slot_to_token, -7)
     qt, kt, vt = (torch.zeros_like(L.qt) for _ in range(3))
     pooled = torch.full_like(L.pooled, float("nan"))
     scores = torch.full_like(L.scores, float("nan"))
-    vsa.vsa_map_tiles_scores(run.prob, run.q, run.k, run.v, s2t, qt, kt, vt, run.wq, run.wk,
-                             pooled, scores)
+    vsa.vsa_map_tiles_scores(run.prob, L.mode, L.proj_dim, run.q, run.k, run.v, s2t, qt, kt, vt,
+                             run.wq, run.wk, pooled, scores)
     torch.cuda.synchronize()
     sz = L.sizes
     assert torch.equal(s2t, L.slot_to_token)
     per_head = sz.max_tiles * 64 * w.d
     nv, BH = sz.max_video_tiles, w.B * w.H
+    r = vsa.vsa_pooled_bytes(run.prob, L.mode, L.proj_dim) // (8 * 2 * BH * nv)
     sc_a, sc_b = L.scores.view(BH, nv, nv), scores.view(BH, nv, nv)
-    pd_a = L.pooled[: 2 * BH * nv * w.d].view(2, BH, nv, w.d)
-    pd_b = pooled[: 2 * BH * nv * w.d].view(2, BH, nv, w.d)
+    pd_a = L.pooled[: 2 * BH * nv * r].view(2, BH, nv, r)
+    pd_b = pooled[: 2 * BH * nv * r].view(2, BH, nv, r)
     for bh in range(BH):
         si = (bh % w.H) % len(w.tile_shapes)
         nt, n = sz.n_tiles[si], sz.n_video_tiles[si]

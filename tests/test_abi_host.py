@@ -499,14 +499,17 @@ def test_map_tiles_scores_rejects_before_launch():
     L = vsa.lib()
     fake, odd = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x10008)
     p = _problem(WORKLOADS["1"])
-    f = lambda **kw: L.vsa_map_tiles_scores(
-        p.ref, kw.get("q", fake), kw.get("k", fake), kw.get("v", fake), kw.get("s2t", fake),
-        kw.get("qt", fake), kw.get("kt", fake), kw.get("vt", fake), kw.get("wq", fake), None,
-        kw.get("ws", fake), kw.get("sc", fake), None)
+    f = lambda mode=0, proj=p.d, **kw: L.vsa_map_tiles_scores(
+        p.ref, mode, proj, kw.get("q", fake), kw.get("k", fake), kw.get("v", fake),
+        kw.get("s2t", fake), kw.get("qt", fake), kw.get("kt", fake), kw.get("vt", fake),
+        kw.get("wq", fake), kw.get("wk", None), kw.get("ws", fake), kw.get("sc", fake), None)
     odd4 = ctypes.c_void_p(0x10004)         # workspace of doubles: 8-byte alignment
     for kw in (dict(q=None), dict(k=None), dict(s2t=None), dict(qt=None), dict(wq=None),
                dict(ws=None), dict(sc=None), dict(vt=None), dict(q=odd), dict(ws=odd4)):
         assert f(**kw) == vsa.VSA_ERR_INVALID_ARG, kw
+    assert f(mode=1, proj=32) == vsa.VSA_ERR_INVALID_ARG          # TripPool needs wk
+    assert f(mode=1, proj=24, wk=fake) == vsa.VSA_ERR_UNSUPPORTED  # not a power of two
+    assert f(mode=0, proj=32) == vsa.VSA_ERR_INVALID_ARG          # mean gate: proj_dim = d
     bad = _problem(WORKLOADS["1"], d=96)
-    assert L.vsa_map_tiles_scores(bad.ref, fake, fake, fake, fake, fake, fake, fake, fake, None,
-                                  fake, fake, None) == vsa.VSA_ERR_UNSUPPORTED
+    assert L.vsa_map_tiles_scores(bad.ref, 0, 96, fake, fake, fake, fake, fake, fake, fake, fake,
+                                  None, fake, fake, None) == vsa.VSA_ERR_UNSUPPORTED

@@ -132,11 +132,11 @@ def test_fused_select_equals_two_calls(run):
 
 
 def test_gather_pool_equals_two_calls(run):
-    """Mean-gate workloads: vsa_map_tiles_scores writes exactly what
-    vsa_map_tiles + vsa_tile_scores write (checked against the oracle above)."""
+    """vsa_map_tiles_scores writes exactly what vsa_map_tiles +
+    vsa_tile_scores write (checked against the oracle above), for the mean
+    gate and for TripPool."""
     gs.log(f"[parity] one-pass gather and pooling {run.name}")
-    done = gs.assert_gather_pool_equal(run)
-    assert done == (run.w.scorer == "mean_gate")
+    assert gs.assert_gather_pool_equal(run)
 
 
 def _pick_tiles(tm, count, seed):

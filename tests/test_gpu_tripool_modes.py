@@ -72,6 +72,8 @@ def test_tripool_mode_parity(dt, mode):
                 assert mx <= gs.F32_MAX_ABS
             else:
                 assert mx <= gs.BF16_MAX_ABS and mean <= gs.BF16_MEAN_ABS
+    # the one-pass gather and pooling writes the same tiles, descriptors and scores
+    assert gs.assert_gather_pool_equal(r)
 
 
 @pytest.mark.parametrize("mode", ["maxmin", "avg"])
