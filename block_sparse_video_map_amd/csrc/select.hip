@@ -125,7 +125,8 @@ __global__ __launch_bounds__(kSelThreads) void select_wave_kernel(Plan p, Select
     const uint64_t eqm = __ballot(key[e] == T);
     const bool keep = key[e] > T || (key[e] == T && ties + bits_below(eqm) < need);
     const uint64_t km = __ballot(keep);
-    if (keep) out[base + bits_below(km)] = e * 64 + lane;
+    const int pos = base + bits_below(km);
+    if (keep && pos < k) out[pos] = e * 64 + lane;           // always: k kept
     base += __builtin_popcountll(km);
     ties += __builtin_popcountll(eqm);
   }
@@ -264,7 +265,10 @@ __global__ __launch_bounds__(kSelThreads) void select_block_kernel(Plan p, Selec
         keep = eq_rank < need;
         ++eq_rank;
       }
-      if (keep) out[pos++] = j0 + e;
+      if (keep) {
+        if (pos < k) out[pos] = j0 + e;                       // always: k kept
+        ++pos;
+      }
     }
   }
   for (int c = k + t; c < job.out_row; c += kSelThreads) out[c] = -1;
