@@ -1,17 +1,12 @@
 // Step 4 (bf16): tile-skipping flash attention on the 32x32x16 bf16 MFMA.
 //
 // Work unit: a workgroup of eight waves takes two neighbouring query tiles
-// of one head, A and B (prefix query tiles pair with prefix query tiles and
-// video with video; an odd one out goes alone). A query tile's key list (all
-// prefix tiles, then its kept video tiles; every tile for a prefix query
-// tile) is cut into 32-key units, and units without a real key are dropped.
-// A unit both tiles keep is one shared step; the i-th unit only A keeps and
-// the i-th unit only B keeps form one paired step. Every wave therefore has
-// work in every step, and each K/V byte a shared step copies serves both
-// tiles (neighbouring tiles share most of their kept tiles). Membership
-// comes from a bitmap of each row's tiles, so the order of the indices does
-// not matter. Steps are dealt round-robin to two key splits; a split is four
-// waves (two tiles x two 32-query halves), one per SIMD.
+// of one head, with their key lists cut into 32-key units and merged into
+// shared and paired steps (attn_pairs.h). Every wave therefore has work in
+// every step, and each K/V byte a shared step copies serves both tiles
+// (neighbouring tiles share most of their kept tiles). Steps are dealt
+// round-robin to two key splits; a split is four waves (two tiles x two
+// 32-query halves), one per SIMD.
 //
 // A split's K and V go through two-slot LDS rings filled by direct-to-LDS
 // buffer loads (each of the four waves copies its share; no registers held
@@ -37,10 +32,10 @@
 //
 // Workgroups are renumbered so that each of the eight XCDs (which receive
 // workgroup ids round-robin) walks a contiguous run of query-tile pairs.
-#include <algorithm>
 #include <cstdlib>
 
 #include "attn_common.h"
+#include "attn_pairs.h"
 #include "kernels.h"
 
 namespace vsa {
@@ -49,11 +44,12 @@ namespace {
 constexpr int kSplits = 2;                       // key splits per workgroup
 constexpr int kWaves = 8;                        // splits x two tiles x two query halves
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowCap = 1024;                    // key tiles per row of a merged pair list
+using pairs::kNone;
+using pairs::kRowCap;
+using pairs::PairGrid;
 constexpr int kStepCap = 4 * kRowCap;            // steps per chunk
 constexpr int kStepStride = kStepCap / kSplits;  // steps per split
 constexpr int kChunkTiles = kStepCap / 2;        // key tiles per chunk of a shared list
-constexpr uint32_t kNone = 0xFFFF;               // no unit for this tile in a step
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -1.0e30f;
@@ -62,15 +58,6 @@ constexpr int kGuard = 1 << 20;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Query tiles per workgroup: pairs of neighbouring query tiles of one head.
-struct PairGrid {
-  int32_t n_wg[VSA_MAX_SHAPES];   // workgroups per head of each shape
-  int64_t wg_per_cycle;           // over one cycle of shapes
-  int64_t wg_per_batch;
-  int32_t total;
-  int32_t pair_video;             // video query rows are paired (their lists fit)
-};
 
 __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -87,74 +74,6 @@ __device__ inline void copy4k(__amdgpu_buffer_rsrc_t r, lds_ptr_t dst, int voff,
 __device__ inline void copy2k(__amdgpu_buffer_rsrc_t r, lds_ptr_t dst, int voff, int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 1024, 0);
-}
-
-__device__ inline int lanes_below(uint64_t m) {
-  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
-// Real keys among the 32 slots of key half kb of `tile` (shape s).
-__device__ inline int unit_real(const Plan &p, int s, int tile, int kb) {
-  if (tile < p.n_prefix_tiles) {
-    int seg = 0;
-    while (seg + 1 < p.n_prefix && tile >= p.prefix_tile0[seg + 1]) ++seg;
-    const int r = p.prefix_len[seg] - (tile - p.prefix_tile0[seg]) * kTile - 32 * kb;
-    return r < 0 ? 0 : (r > 32 ? 32 : r);
-  }
-  if (p.video_full[s]) return 32;
-  const int v = tile - p.n_prefix_tiles;
-  const int gw = p.grid_w[s], gh = p.grid_h[s];
-  const int wi = v % gw, hi = (v / gw) % gh, ti = v / (gw * gh);
-  const int pt = p.shape[s][0], ph = p.shape[s][1], pw = p.shape[s][2];
-  const int rt = min(pt, p.T - ti * pt), rh = min(ph, p.Hv - hi * ph), rw = min(pw, p.Wv - wi * pw);
-  if (rt == pt && rh == ph && rw == pw) return 32;
-  int n = 0;
-  for (int j = 0; j < 32; ++j) {
-    const int slot = kb * 32 + j;
-    const int a = slot / (ph * pw), bb = (slot / pw) % ph, c = slot % pw;
-    n += (a < rt) & (bb < rh) & (c < rw);
-  }
-  return n;
-}
-
-// Query tiles tA, tB (tB < 0: none) of workgroup blockIdx.x, XCD-aware
-// numbering as in work_item.
-__device__ inline void pair_item(const Plan &p, const PairGrid &gd, int &b, int &h, int &tA,
-                                 int &tB) {
-  const int i = blockIdx.x;
-  const int q8 = gd.total / 8;
-  const int L = i < 8 * q8 ? (i % 8) * q8 + i / 8 : i;
-  b = (int)(L / gd.wg_per_batch);
-  const int64_t rem = L % gd.wg_per_batch;
-  const int cyc = (int)(rem / gd.wg_per_cycle);
-  int r = (int)(rem % gd.wg_per_cycle);
-  int s = 0;
-  while (r >= gd.n_wg[s]) {
-    r -= gd.n_wg[s];
-    ++s;
-  }
-  h = cyc * p.n_shapes + s;
-  const int npt = p.n_prefix_tiles;
-  if (p.dense) {
-    tA = 2 * r;
-    tB = tA + 1 < p.n_tiles[s] ? tA + 1 : -1;
-    return;
-  }
-  const int npw = (npt + 1) / 2;
-  if (r < npw) {
-    tA = 2 * r;
-    tB = tA + 1 < npt ? tA + 1 : -1;
-    return;
-  }
-  const int v = r - npw;
-  if (gd.pair_video) {
-    tA = npt + 2 * v;
-    tB = 2 * v + 1 < p.n_vt[s] ? tA + 1 : -1;
-  } else {
-    tA = npt + v;
-    tB = -1;
-  }
 }
 
 // Softmax probabilities of one unit against the running max m (log2 units),
@@ -235,7 +154,7 @@ void attn_bf16_kernel(Plan p, PairGrid gd, const bf16_bits *__restrict__ qt,
   __shared__ int fault;
 
   int b, h, tA, tB;
-  pair_item(p, gd, b, h, tA, tB);
+  pairs::pair_item(p, gd, b, h, tA, tB);
   const int s = h % p.n_shapes;
   const int bh = b * p.H + h;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
@@ -321,163 +240,9 @@ void attn_bf16_kernel(Plan p, PairGrid gd, const bf16_bits *__restrict__ qt,
     asm volatile("" ::: "memory");
   };
 
-  // ---- step lists. A step gives each of the two tiles one 32-key unit
-  // (entry = tile*2 + half, bit 15 for a partly padded half; kNone: none);
-  // both tiles get the same unit when they share it. Step j goes to split
-  // j % 2.
-  auto put_step = [&](int j, uint32_t eA, uint32_t eB) {
-    steps[(j % kSplits) * kStepStride + j / kSplits] = eA | (eB << 16);
-  };
-  // Units of A's entries [e0, e1) as shared steps (both tiles take them).
-  auto build_shared = [&](int e0, int e1) -> int {
-    const int32_t *kv_row = fullA ? nullptr : kv_row_of(tA);
-    const int32_t *ref_row = fullA ? nullptr : ref_row_of(tA);
-    int base = 0;
-    for (int r0 = e0; r0 < e1; r0 += kThreads) {
-      const int e = r0 + (int)threadIdx.x;
-      int tile = -1, n0 = 0, n1 = 0;
-      if (e < e1) {
-        tile = fullA ? e : video_row_tile(p, s, e, kv_row, ref_row);
-        if (tile >= 0) {
-          n0 = unit_real(p, s, tile, 0);
-          n1 = unit_real(p, s, tile, 1);
-        }
-      }
-      const uint64_t b1 = __ballot(n0 > 0 || n1 > 0);
-      const uint64_t b2 = __ballot(n0 > 0 && n1 > 0);
-      const int pre = lanes_below(b1) + lanes_below(b2);
-      if (lane == 0) scan[wave] = __builtin_popcountll(b1) + __builtin_popcountll(b2);
-      __syncthreads();
-      int woff = 0, tot = 0;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const int c = scan[w];
-        woff += w < wave ? c : 0;
-        tot += c;
-      }
-      int pos = base + woff + pre;
-      if (n0 > 0) {
-        const uint32_t u = (uint32_t)(tile * 2) | (n0 < 32 ? 0x8000u : 0u);
-        put_step(pos++, u, u);
-      }
-      if (n1 > 0) {
-        const uint32_t u = (uint32_t)(tile * 2 + 1) | (n1 < 32 ? 0x8000u : 0u);
-        put_step(pos, u, u);
-      }
-      base += tot;
-      __syncthreads();
-    }
-    return base;
-  };
-  // Two video rows: units both rows keep are shared steps; the i-th unit only
-  // A keeps and the i-th unit only B keeps make one step. Membership comes
-  // from a bitmap of each row's tiles (LDS, in the K slots before any copy).
-  auto build_merged = [&]() -> int {
-    uint32_t *bmA = reinterpret_cast<uint32_t *>(kslot0);
-    uint32_t *bmB = bmA + (p.max_tiles + 31) / 32;
-    const int words = (p.max_tiles + 31) / 32;
-    for (int i = threadIdx.x; i < 2 * words; i += kThreads) bmA[i] = 0u;
-    __syncthreads();
-    const int n_kv = video_row_len(p, s);
-    const int32_t *kvA = kv_row_of(tA), *kvB = kv_row_of(tB);
-    const int32_t *rfA = ref_row_of(tA), *rfB = ref_row_of(tB);
-    for (int e = threadIdx.x; e < n_kv; e += kThreads) {
-      const int ta = video_row_tile(p, s, e, kvA, rfA), tbb = video_row_tile(p, s, e, kvB, rfB);
-      if (ta >= 0) atomicOr(&bmA[ta >> 5], 1u << (ta & 31));
-      if (tbb >= 0) atomicOr(&bmB[tbb >> 5], 1u << (tbb & 31));
-    }
-    __syncthreads();
-    int nA = 0, nxA = 0;
-    for (int r0 = 0; r0 < n_kv; r0 += kThreads) {
-      const int e = r0 + (int)threadIdx.x;
-      int tile = -1, n0 = 0, n1 = 0;
-      bool shared = false;
-      if (e < n_kv) {
-        tile = video_row_tile(p, s, e, kvA, rfA);
-        if (tile >= 0) {
-          n0 = unit_real(p, s, tile, 0);
-          n1 = unit_real(p, s, tile, 1);
-          shared = (bmB[tile >> 5] >> (tile & 31)) & 1u;
-        }
-      }
-      const int cnt = (n0 > 0) + (n1 > 0), xc = shared ? 0 : cnt;
-      const uint64_t b1 = __ballot(cnt >= 1), b2 = __ballot(cnt >= 2);
-      const uint64_t x1 = __ballot(xc >= 1), x2 = __ballot(xc >= 2);
-      const int pre = lanes_below(b1) + lanes_below(b2);
-      const int xpre = lanes_below(x1) + lanes_below(x2);
-      if (lane == 0) {
-        scan[wave] = __builtin_popcountll(b1) + __builtin_popcountll(b2);
-        scan[kWaves + wave] = __builtin_popcountll(x1) + __builtin_popcountll(x2);
-      }
-      __syncthreads();
-      int woff = 0, tot = 0, xoff = 0, xtot = 0;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const int c = scan[w], x = scan[kWaves + w];
-        woff += w < wave ? c : 0;
-        tot += c;
-        xoff += w < wave ? x : 0;
-        xtot += x;
-      }
-      int pos = nA + woff + pre, xr = nxA + xoff + xpre;
-      if (n0 > 0) {
-        const uint32_t u = (uint32_t)(tile * 2) | (n0 < 32 ? 0x8000u : 0u);
-        ulA[pos++] = u | (shared ? 0u : (uint32_t)(xr++ + 1) << 16);
-      }
-      if (n1 > 0) {
-        const uint32_t u = (uint32_t)(tile * 2 + 1) | (n1 < 32 ? 0x8000u : 0u);
-        ulA[pos] = u | (shared ? 0u : (uint32_t)(xr + 1) << 16);
-      }
-      nA += tot;
-      nxA += xtot;
-      __syncthreads();
-    }
-    int nxB = 0;
-    for (int r0 = 0; r0 < n_kv; r0 += kThreads) {
-      const int e = r0 + (int)threadIdx.x;
-      int tile = -1, n0 = 0, n1 = 0;
-      if (e < n_kv) {
-        tile = video_row_tile(p, s, e, kvB, rfB);
-        if (tile >= 0 && !((bmA[tile >> 5] >> (tile & 31)) & 1u)) {
-          n0 = unit_real(p, s, tile, 0);
-          n1 = unit_real(p, s, tile, 1);
-        }
-      }
-      const uint64_t b1 = __ballot(n0 > 0 || n1 > 0);
-      const uint64_t b2 = __ballot(n0 > 0 && n1 > 0);
-      const int pre = lanes_below(b1) + lanes_below(b2);
-      if (lane == 0) scan[wave] = __builtin_popcountll(b1) + __builtin_popcountll(b2);
-      __syncthreads();
-      int woff = 0, tot = 0;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const int c = scan[w];
-        woff += w < wave ? c : 0;
-        tot += c;
-      }
-      int pos = nxB + woff + pre;
-      if (n0 > 0) bx[pos++] = (uint16_t)((tile * 2) | (n0 < 32 ? 0x8000 : 0));
-      if (n1 > 0) bx[pos] = (uint16_t)((tile * 2 + 1) | (n1 < 32 ? 0x8000 : 0));
-      nxB += tot;
-      __syncthreads();
-    }
-    const int nS = nA + max(0, nxB - nxA);
-    for (int i = threadIdx.x; i < nS; i += kThreads) {
-      uint32_t eA, eB;
-      if (i < nA) {
-        const uint32_t a = ulA[i];
-        eA = a & 0xFFFFu;
-        const uint32_t x = a >> 16;
-        eB = x == 0 ? eA : (x - 1 < (uint32_t)nxB ? (uint32_t)bx[x - 1] : kNone);
-      } else {
-        eA = kNone;
-        eB = bx[nxA + (i - nA)];
-      }
-      put_step(i, eA, eB);
-    }
-    __syncthreads();
-    return nS;
-  };
+  // ---- step lists (attn_pairs.h): 32-key units, step j to split j % 2.
+  // The merged build keeps its tile bitmaps in the K slots before any copy.
+  const pairs::ListSmem lsm{steps, ulA, bx, scan, reinterpret_cast<uint32_t *>(kslot0)};
 
   const uint32_t *mysteps = steps + sp * kStepStride;
   auto step_at = [&](int j) -> uint32_t {
@@ -546,7 +311,12 @@ void attn_bf16_kernel(Plan p, PairGrid gd, const bf16_bits *__restrict__ qt,
   const int n_rows = merge ? 1 : (fullA ? p.n_tiles[s] : video_row_len(p, s));
   const int chunk = merge ? n_rows : kChunkTiles;
   for (int e0 = 0; e0 < n_rows; e0 += chunk) {
-    const int nS = merge ? build_merged() : build_shared(e0, min(n_rows, e0 + chunk));
+    const int nS =
+        merge ? pairs::build_merged<2, kWaves, kSplits, kStepStride>(
+                    p, s, kv_row_of(tA), ref_row_of(tA), kv_row_of(tB), ref_row_of(tB), lsm)
+              : pairs::build_shared<2, kWaves, kSplits, kStepStride>(
+                    p, s, fullA, fullA ? nullptr : kv_row_of(tA), fullA ? nullptr : ref_row_of(tA),
+                    e0, min(n_rows, e0 + chunk), lsm);
     const int n_u = nS > sp ? (nS - sp + kSplits - 1) / kSplits : 0;
     if (n_u > 0) {
       // Step u: K in slot u%2 of the K slots, V in slot u%2 of the V slots.
@@ -773,33 +543,12 @@ void attn_bf16_kernel(Plan p, PairGrid gd, const bf16_bits *__restrict__ qt,
   }
 }
 
-PairGrid make_grid(const Plan &p) {
-  PairGrid g{};
-  int longest = 0;
-  for (int s = 0; s < p.n_shapes; ++s)
-    longest = std::max(longest, p.n_prefix_tiles - p.n_ref + p.k_ref + p.k[s]);
-  g.pair_video = !p.dense && longest <= kRowCap;
-  for (int s = 0; s < p.n_shapes; ++s) {
-    if (p.dense) {
-      g.n_wg[s] = (p.n_tiles[s] + 1) / 2;
-    } else {
-      g.n_wg[s] = (p.n_prefix_tiles + 1) / 2 + (g.pair_video ? (p.n_vt[s] + 1) / 2 : p.n_vt[s]);
-    }
-  }
-  g.wg_per_cycle = 0;
-  for (int s = 0; s < p.n_shapes; ++s) g.wg_per_cycle += g.n_wg[s];
-  g.wg_per_batch = 0;
-  for (int h = 0; h < p.H; ++h) g.wg_per_batch += g.n_wg[h % p.n_shapes];
-  g.total = (int32_t)(g.wg_per_batch * p.B);
-  return g;
-}
-
 }  // namespace
 
 hipError_t launch_attn_bf16(const Plan &p, const void *qt, const void *kt, const void *vt,
                             const int32_t *s2t, const int32_t *kv_idx, const int32_t *ref_idx,
                             float scale, void *out, float *lse, hipStream_t stream) {
-  const PairGrid gd = make_grid(p);
+  const PairGrid gd = pairs::make_grid(p);
   const float sl2 = scale * kLog2e;
   if (p.d == 128)
     hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(gd.total), dim3(kThreads), 0, stream, p, gd,

@@ -8,15 +8,16 @@
 // through its scale operand (an exact 2^(e) factor), so S = Q K^T and the
 // PV product see the dequantized values.
 //
-// The bf16 kernel's work split with two key splits instead of four: one
-// 64-token query tile per workgroup of four waves, two key splits of two
-// waves (one per 32-query half), two workgroups per CU. Each split has a
-// two-slot LDS ring filled by direct-to-LDS buffer loads (wave 0 the K tile,
-// wave 1 the V tile) and one barrier per key tile. A whole 64-key tile is one
-// unit here: K and V of a tile are 8 KB each at d = 128. With half the bytes
-// per key tile of the bf16 path, fewer splits per workgroup (less coupling at
-// the barrier) measured faster than four, while the bf16 kernel keeps four
-// (its L2 reuse across neighbouring query tiles matters more there).
+// Work split as in the bf16 kernel: a workgroup of eight waves takes two
+// neighbouring query tiles whose key lists are merged into shared and
+// paired steps (attn_pairs.h), dealt to two key splits of four waves (two
+// tiles x two 32-query halves). A unit is a whole 64-key tile here, because
+// the PV product sums over 64 keys per instruction; its K and its V are
+// 8 KiB each at d = 128, the size of a bf16 half-tile unit. K is copied into
+// a two-slot LDS ring two steps ahead of use and V one step ahead, by
+// direct-to-LDS buffer loads; the four waves of a split wait for each other
+// once per step (bounded; a wave that gives up makes the workgroup write
+// NaN).
 //
 // Products are taken transposed, S^T = K Q^T and O^T = V^T P^T, so a lane
 // owns one query column. The probabilities are packed to E4M3 in the order
@@ -24,29 +25,43 @@
 // stores keys in, so P^T is the B operand of the PV product as it stands.
 // Row sums are taken over the same rounded probabilities, by one more MFMA
 // against an all-ones A operand, so numerator and denominator use the same
-// weights.
+// weights. A step issues its nine MFMAs (the PV product and row sum of the
+// previous unit alternating with the S^T product of the next) with the
+// current unit's softmax spread between them.
 //
 // The running max m is an integer in log2 units, set 8 below the row max, so
 // that probabilities lie in (0, 2^8] and use the whole E4M3 range (largest
 // value 448; normal down to 2^-6). It is raised only when a unit holds a
-// logit more than 8 above it; then O and the row sum are rescaled first.
+// logit more than 8 above it. The test runs at the end of the step that
+// computes the unit's S^T, outside the MFMA sequence: O and the row sums
+// are rescaled there by the exact power of two, and the probabilities still
+// waiting for their PV product (formed against the old max) take the same
+// factor through the product's per-column B scale.
 #include <cstdlib>
 
 #include "attn_common.h"
+#include "attn_pairs.h"
 #include "fp8_layout.h"
 #include "kernels.h"
 
 namespace vsa {
 namespace {
 
-constexpr int kSplits = 2;                   // key splits per query tile
-constexpr int kWaves = 2 * kSplits;          // two query halves per split
+constexpr int kSplits = 2;                       // key splits per workgroup
+constexpr int kWaves = 8;                        // splits x two tiles x two query halves
 constexpr int kThreads = 64 * kWaves;
+using pairs::kNone;
+using pairs::kRowCap;
+using pairs::PairGrid;
+constexpr int kStepCap = 2 * kRowCap;            // steps per chunk (one unit per key tile)
+constexpr int kStepStride = kStepCap / kSplits;  // steps per split
+constexpr int kChunkTiles = kStepCap;            // key tiles per chunk of a shared list
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegBig = -1.0e30f;
-constexpr float kSlack = 8.0f;               // probabilities <= 2^kSlack
-constexpr int kOne = kFp8ExpBias;            // scale byte of 2^0
+constexpr float kSlack = 8.0f;                   // probabilities <= 2^kSlack
+constexpr int kOne = kFp8ExpBias;                // scale byte of 2^0
+constexpr int kGuard = 1 << 20;
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -61,53 +76,115 @@ __device__ inline i32x8 join(i32x4 lo, i32x4 hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// The 32-byte operand of this lane in a 2 KB block (two halves 1 KB apart).
+// The 32-byte operand of this lane in a 2 KiB block (two halves 1 KiB apart).
 __device__ inline i32x8 lds_operand(const uint8_t *blk, int lane) {
   return join(*reinterpret_cast<const i32x4 *>(blk + lane * 16),
               *reinterpret_cast<const i32x4 *>(blk + 1024 + lane * 16));
 }
 
+// N consecutive 1 KiB blocks to LDS (N <= 4: one LDS base, instruction
+// offsets move source and destination alike).
+template <int N>
+__device__ inline void copy_kib(__amdgpu_buffer_rsrc_t r, lds_ptr_t dst, int voff, int soff) {
+  static_assert(N == 2 || N == 4, "two or four blocks");
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 1024, 0);
+  if (N == 4) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 2048, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 3072, 0);
+  }
+}
+
+// Counts as a use of x (in VGPRs) at this point, so that its computation
+// stays before it. (The host pass, which never runs kernel code, sees an
+// empty body: "v" is a GPU register constraint.)
+template <typename T>
+__host__ __device__ __forceinline__ void keep_here(const T &x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" ::"v"(x));
+#else
+  (void)x;
+#endif
+}
+
+// Real-key mask of unit entry e (bit = key slot 0..63); 0 for no unit.
+__device__ __forceinline__ uint64_t unit_mask(const Plan &p, int s, uint32_t e, int lane) {
+  if (e == kNone) return 0ull;
+  return __ballot(slot_token(p, s, (int)(e & 0x7FFF), lane) >= 0);
+}
+
+// Element r of block kb of lane (g, l32) of S^T is key kb*32 + (r/4)*8 + g*4 + r%4:
+// after one shift by 4g, a fixed bit per element.
+__device__ __forceinline__ void mask_keys(f32x16 (&sc)[2], uint64_t m, int g) {
+  const uint64_t mg = m >> (4 * g);
+  const uint32_t lo = (uint32_t)mg, hi = (uint32_t)(mg >> 32);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int bit = (r / 4) * 8 + (r % 4);
+      sc[kb][r] = (((kb ? hi : lo) >> bit) & 1u) ? sc[kb][r] : -INFINITY;
+    }
+}
+
+// Four probabilities of elements r0..r0+3 of block kb against the max m,
+// packed to E4M3: byte e = 4j + t of the P^T operand is element 4*(j%4) + t
+// of block j/4.
+__device__ __forceinline__ int probs4(const f32x16 &blk, int r0, float scale_log2, float m) {
+  float pv[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) pv[t] = __builtin_amdgcn_exp2f(fmaf(blk[r0 + t], scale_log2, -m));
+  return (int)fp8_pack4(pv[0], pv[1], pv[2], pv[3]);
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_fp8_kernel(Plan p, int total, const uint8_t *__restrict__ q8,
+void attn_fp8_kernel(Plan p, PairGrid gd, const uint8_t *__restrict__ q8,
                      const uint8_t *__restrict__ k8, const uint8_t *__restrict__ v8,
                      const uint32_t *__restrict__ scales, const int32_t *__restrict__ s2t,
                      const int32_t *__restrict__ kv_idx, const int32_t *__restrict__ ref_idx,
                      float scale_log2, bf16_bits *__restrict__ out, float *__restrict__ lse) {
   constexpr int NCH = D / 64, NDB = D / 32;
-  constexpr int TB = kTile * D;                // bytes of one fp8 tile
-  // Two slots per split, each K then V of one key tile. Distinct objects: a
-  // slot is only read while the other one is being filled.
-  __shared__ __attribute__((aligned(1024))) uint8_t ring0_all[kSplits * 2 * TB];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring1_all[kSplits * 2 * TB];
+  constexpr int TB = kTile * D;                // bytes of one fp8 tile (the unit)
+  constexpr int SLOT = 2 * TB;                 // a split's slot: two units (tile A, tile B)
+  constexpr int NS = 2 * NCH;                  // S^T products per unit
+  constexpr int NP = NDB + 1;                  // PV products and the row sum
+  constexpr int NSLOT = NS + NP;               // MFMA issue slots of a step
+  __shared__ __attribute__((aligned(1024))) uint8_t kslot0[kSplits * SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t kslot1[kSplits * SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t vslot0[kSplits * SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t vslot1[kSplits * SLOT];
+  __shared__ uint32_t steps[kStepCap];
+  __shared__ uint32_t ulA[kRowCap];
+  __shared__ uint16_t bx[kRowCap];
+  __shared__ __attribute__((aligned(16))) int grp_count[kSplits * 4];
+  __shared__ int scan[2 * kWaves];
+  __shared__ int fault;
 
-  int b, h, tq;
-  work_item(p, total, b, h, tq);
+  int b, h, tA, tB;
+  pairs::pair_item(p, gd, b, h, tA, tB);
   const int s = h % p.n_shapes;
   const int bh = b * p.H + h;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
-  const int qb = wave % 2, ks = wave / 2;
-  uint8_t *const ring0 = ring0_all + ks * 2 * TB;
-  uint8_t *const ring1 = ring1_all + ks * 2 * TB;
+  const int sp = wave / 4, role = wave % 4;     // split; role = tile*2 + query half
+  const int tb = role / 2, qb = role % 2;
+  const int myT = tb ? tB : tA;
   const int lane = threadIdx.x % 64;
   const int g = lane / 32, l32 = lane % 32;
   const int npt = p.n_prefix_tiles;
-  const bool full_row = p.dense || tq < npt;
-  const int n_kv = full_row ? p.n_tiles[s] : video_row_len(p, s);
-  // Key lists and scale words are read through the constant address space
-  // (scalar loads), off the vector-memory counter of the copies.
-  typedef const __attribute__((address_space(4))) int32_t *const_i32_ptr;
-  typedef const __attribute__((address_space(4))) uint32_t *const_u32_ptr;
-  const const_i32_ptr kv_row =
-      full_row ? nullptr
-               : (const_i32_ptr)(kv_idx + ((int64_t)bh * p.max_vt + (tq - npt)) * p.k_max);
-  const const_i32_ptr ref_row =
-      (full_row || p.n_ref == 0)
-          ? nullptr
-          : (const_i32_ptr)(ref_idx + ((int64_t)bh * p.max_vt + (tq - npt)) * p.k_ref);
+  const bool fullA = p.dense || tA < npt;
+  const bool merge = tB >= 0 && !fullA;         // two video rows with their own lists
   const int64_t head_base = (int64_t)bh * p.max_tiles;
-  const const_u32_ptr sc_row = (const_u32_ptr)(scales + head_base);
   const int32_t *map = s2t + (int64_t)s * p.max_tiles * kTile;
+  auto kv_row_of = [&](int t) {
+    return kv_idx + ((int64_t)bh * p.max_vt + (t - npt)) * p.k_max;
+  };
+  auto ref_row_of = [&](int t) -> const int32_t * {
+    return p.n_ref == 0 ? nullptr : ref_idx + ((int64_t)bh * p.max_vt + (t - npt)) * p.k_ref;
+  };
+  // Scale words are read through the constant address space (scalar loads).
+  typedef const __attribute__((address_space(4))) uint32_t *const_u32_ptr;
+  const const_u32_ptr sc_row = (const_u32_ptr)(scales + head_base);
 
   const uint32_t head_bytes = (uint32_t)p.max_tiles * TB;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(q8 + head_base * TB, head_bytes);
@@ -115,14 +192,33 @@ void attn_fp8_kernel(Plan p, int total, const uint8_t *__restrict__ q8,
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(v8 + head_base * TB, head_bytes);
   const int voff = lane * 16;
 
+  if (threadIdx.x < kSplits * 4) grp_count[threadIdx.x] = 0;
+  if (threadIdx.x == 0) fault = 0;
+  // A wave whose tile has no unit in a paired step (entry kNone) still runs
+  // its PV products, with every probability zero, on its tile's half of the
+  // V slot, which this kernel may not have written yet. LDS keeps what an
+  // earlier kernel left there, possibly E4M3 NaN codes, and 0 * NaN = NaN; so
+  // the V rings start zeroed. The barriers of the list building order these
+  // stores before the first copy into the rings.
+  {
+    const i32x4 z = {0, 0, 0, 0};
+    i32x4 *v0 = reinterpret_cast<i32x4 *>(vslot0), *v1 = reinterpret_cast<i32x4 *>(vslot1);
+    for (int x = threadIdx.x; x < kSplits * SLOT / 16; x += kThreads) {
+      v0[x] = z;
+      v1[x] = z;
+    }
+  }
+
   i32x8 qf[NCH];              // this wave's Q^T operands (B of S^T = K Q^T)
+  const int qtile = myT >= 0 ? myT : tA;
 #pragma unroll
   for (int cc = 0; cc < NCH; ++cc) {
-    const int base = tq * TB + (qb * NCH + cc) * 2048;
+    const int base = qtile * TB + (qb * NCH + cc) * 2048;
     qf[cc] = join(__builtin_amdgcn_raw_buffer_load_b128(rq, voff, base, 0),
                   __builtin_amdgcn_raw_buffer_load_b128(rq, voff, base + 1024, 0));
   }
-  const int sq = (int)(sc_row[tq] & 0xFFu);
+  const int sq = (int)(sc_row[qtile] & 0xFFu);
+  const bool q_live = myT >= 0 && __any(map[(int64_t)myT * kTile + qb * 32 + l32] >= 0);
   const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                       0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
   f32x16 o[NDB], lsum;
@@ -133,160 +229,285 @@ void attn_fp8_kernel(Plan p, int total, const uint8_t *__restrict__ q8,
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
   float m_use = kNegBig;
+  bool stalled = false;
+  int sync_n = 0;
 
-  // Global tile of this split's i-th key tile; ok = false for an index
-  // outside the head's video tiles (then the tile is fully masked).
-  const int n_mine = n_kv > ks ? (n_kv - ks + kSplits - 1) / kSplits : 0;
-  auto tile_of = [&](int i, bool &ok) -> int {
-    ok = true;
-    i = ks + kSplits * i;
-    if (full_row) return i;
-    const int tile = video_row_tile(p, s, i, kv_row, ref_row);
-    if (tile < 0) {
-      ok = false;
-      return 0;
+  // The four waves of a split wait for each other once per step (LDS
+  // counters); bounded, and a wave that gives up poisons the outputs.
+  typedef volatile __attribute__((address_space(3))) int *lds_iptr;
+  typedef volatile __attribute__((address_space(3))) i32x4 *lds_i4ptr;
+  const lds_iptr count = (lds_iptr)grp_count;
+  const lds_i4ptr count4 = (lds_i4ptr)(grp_count + sp * 4);
+  auto grp_sync = [&]() {
+    ++sync_n;
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
+    if (lane == 0) count[sp * 4 + role] = sync_n;
+    if (stalled) return;
+    int guard = 0;
+    for (;;) {
+      const i32x4 c = *count4;
+      if (min(min(c.x, c.y), min(c.z, c.w)) >= sync_n) break;
+      if (++guard > kGuard) {
+        stalled = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
     }
-    return tile;
+    asm volatile("" ::: "memory");
   };
-  auto tile_mask = [&](int tile, bool ok) -> uint64_t {
-    if (!ok) return 0ull;
-    if (tile_full(p, s, tile)) return ~0ull;
-    return __ballot(slot_token(p, s, tile, lane) >= 0);
+
+  // Step lists: one unit per key tile; the merged build keeps its tile
+  // bitmaps in the K slots before any copy.
+  const pairs::ListSmem lsm{steps, ulA, bx, scan, reinterpret_cast<uint32_t *>(kslot0)};
+  const uint32_t *mysteps = steps + sp * kStepStride;
+  auto step_at = [&](int j) -> uint32_t {
+    return __builtin_amdgcn_readfirstlane(mysteps[j]);
   };
-  // Copy of key tile `tile` into a slot: wave 0 the K tile, wave 1 the V tile.
-  auto issue = [&](uint8_t *slot, int tile) {
-    const __amdgpu_buffer_rsrc_t r = qb == 0 ? rk : rv;
-    uint8_t *dst = slot + qb * TB;
-#pragma unroll
-    for (int j = 0; j < TB / 1024; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst + j * 1024), 16, voff,
-                                               tile * TB + j * 1024, 0, 0);
+  auto my_unit = [&](uint32_t st) -> uint32_t { return tb ? (st >> 16) : (st & 0xFFFFu); };
+  auto is_shared = [&](uint32_t st) -> bool { return (st & 0xFFFFu) == (st >> 16); };
+  // Scale word of this wave's unit in a step (0 for none: the unit is masked).
+  auto unit_word = [&](uint32_t st) -> uint32_t {
+    const uint32_t e = my_unit(st);
+    const uint32_t w = sc_row[min((int)(e & 0x7FFF), p.max_tiles - 1)];
+    return e == kNone ? 0u : w;
   };
-  // One key tile from a slot: S^T, the mask of a partly filled tile, the
-  // rare raise of the max, E4M3 probabilities, row sums and PV.
-  auto unit = [&](const uint8_t *slot, uint64_t mask, uint32_t word) {
-    const int sk = (int)((word >> 8) & 0xFFu), sv = (int)((word >> 16) & 0xFFu);
-    f32x16 sc[2];
+  // This wave's share of the copies of a step. Shared unit: roles 0 and 1
+  // copy the two halves of K, roles 2 and 3 the two halves of V. Separate
+  // units: role 0 copies A's K, role 1 A's V, role 2 B's K, role 3 B's V
+  // (A's unit at offset 0 of the slot, B's at TB).
+  auto issue_k = [&](uint32_t st, uint8_t *slot_all) __attribute__((always_inline)) {
+    uint8_t *dst = slot_all + sp * SLOT;
+    const uint32_t eA = st & 0xFFFFu, eB = st >> 16;
+    if (eA == eB) {
+      if (role < 2 && eA != kNone) {
+        const int tile = (int)(eA & 0x7FFF);
+        copy_kib<TB / 2048>(rk, (lds_ptr_t)(dst + role * (TB / 2)), voff,
+                            tile * TB + role * (TB / 2));
+      }
+    } else if (role == 0 || role == 2) {
+      const uint32_t e = role == 0 ? eA : eB;
+      if (e != kNone) {
+        const int tile = (int)(e & 0x7FFF);
+        uint8_t *d2 = dst + (role / 2) * TB;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
-#pragma unroll
-      for (int cc = 0; cc < NCH; ++cc)
-        sc[kb] = mfma8(lds_operand(slot + (kb * NCH + cc) * 2048, lane), qf[cc], sc[kb], sk, sq);
+        for (int g4 = 0; g4 < TB / 4096; ++g4)
+          copy_kib<4>(rk, (lds_ptr_t)(d2 + g4 * 4096), voff, tile * TB + g4 * 4096);
+      }
     }
-    if (mask != ~0ull) {
-      // Element r of block kb of lane (g, l32) is key kb*32 + (r/4)*8 + g*4 + r%4.
+  };
+  auto issue_v = [&](uint32_t st, uint8_t *slot_all) __attribute__((always_inline)) {
+    uint8_t *dst = slot_all + sp * SLOT;
+    const uint32_t eA = st & 0xFFFFu, eB = st >> 16;
+    if (eA == eB) {
+      if (role >= 2 && eA != kNone) {
+        const int tile = (int)(eA & 0x7FFF);
+        copy_kib<TB / 2048>(rv, (lds_ptr_t)(dst + (role - 2) * (TB / 2)), voff,
+                            tile * TB + (role - 2) * (TB / 2));
+      }
+    } else if (role == 1 || role == 3) {
+      const uint32_t e = role == 1 ? eA : eB;
+      if (e != kNone) {
+        const int tile = (int)(e & 0x7FFF);
+        uint8_t *d2 = dst + (role / 2) * TB;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + (r / 4) * 8 + g * 4 + (r % 4);
-          sc[kb][r] = ((mask >> key) & 1ull) ? sc[kb][r] : -INFINITY;
-        }
+        for (int g4 = 0; g4 < TB / 4096; ++g4)
+          copy_kib<4>(rv, (lds_ptr_t)(d2 + g4 * 4096), voff, tile * TB + g4 * 4096);
+      }
     }
-    float mt = sc[0][0];
+  };
+  // Operand block blk of this wave's unit in a step's slot.
+  auto unit_off = [&](uint32_t st) -> int { return is_shared(st) ? 0 : tb * TB; };
+  auto frag = [&](const uint8_t *slot_all, int off, int blk) __attribute__((always_inline))
+      -> i32x8 { return lds_operand(slot_all + sp * SLOT + off + blk * 2048, lane); };
+  // Before a unit's softmax: raises the max when some column's logits reach
+  // more than kSlack above it, rescaling O and the row sums (which hold every
+  // unit whose PV product has been issued) and returning in ps the B scale
+  // byte for the probabilities still waiting for theirs (kOne otherwise).
+  auto check_max = [&](const f32x16 (&sc)[2], int &ps) __attribute__((always_inline)) {
+    float mt = fmaxf(sc[0][0], sc[0][1]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[0][r]);
+    for (int r = 2; r < 16; ++r) mt = fmaxf(mt, sc[0][r]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sc[1][r]);
+    ps = kOne;
     if (__builtin_expect(__any(fmaf(mt, scale_log2, -m_use) > kSlack), 0)) {
-      // Move the max to 8 below the unit's row max (both lane halves hold
-      // the same query), rescaling what has been summed so far.
+      // Both lane halves hold the same query column.
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
                                                        false, false);
       const float rm = fmaxf(fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])), mt);
       const float m_new = fmaxf(m_use, ceilf(rm * scale_log2) - kSlack);
       const float alpha = __builtin_amdgcn_exp2f(m_use - m_new);
+      ps = kOne - (int)fminf(m_new - m_use, (float)kOne);
+      m_use = m_new;
 #pragma unroll
       for (int r = 0; r < 16; ++r) lsum[r] *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      m_use = m_new;
     }
-    // Byte e = 4j + t of the P^T operand is element 4*(j%4) + t of block j/4.
-    i32x8 pf;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int kb = j / 4, r0 = 4 * (j % 4);
-      float pv[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        pv[t] = __builtin_amdgcn_exp2f(fmaf(sc[kb][r0 + t], scale_log2, -m_use));
-      pf[j] = (int)fp8_pack4(pv[0], pv[1], pv[2], pv[3]);
-    }
-    lsum = mfma8(ones, pf, lsum, kOne, kOne);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-      o[db] = mfma8(lds_operand(slot + TB + db * 2048, lane), pf, o[db], sv, kOne);
   };
 
-  // Unit i (this split's i-th key tile) uses ring0 for even i, ring1 for
-  // odd i; the copy of unit i + 1 is issued before unit i is computed. Every
-  // wave runs the same number of barriers; a split with fewer tiles idles.
-  const int n_steps = (n_kv + kSplits - 1) / kSplits;
-  bool ok = false;
-  int t = 0;
-  uint64_t mask = 0;
-  uint32_t word = 0;
-  if (n_mine > 0) {
-    t = tile_of(0, ok);
-    word = sc_row[t];
-    mask = tile_mask(t, ok);
-    issue(ring0, t);
-  }
-  sync_slots();
-  for (int i = 0; i < n_steps; i += 2) {
-    bool ok1 = false;
-    int t1 = 0;
-    uint32_t word1 = 0;
-    if (i + 1 < n_mine) {
-      t1 = tile_of(i + 1, ok1);
-      word1 = sc_row[t1];
-      issue(ring1, t1);
+  const int n_rows = merge ? 1 : (fullA ? p.n_tiles[s] : video_row_len(p, s));
+  const int chunk = merge ? n_rows : kChunkTiles;
+  for (int e0 = 0; e0 < n_rows; e0 += chunk) {
+    const int nS =
+        merge ? pairs::build_merged<1, kWaves, kSplits, kStepStride>(
+                    p, s, kv_row_of(tA), ref_row_of(tA), kv_row_of(tB), ref_row_of(tB), lsm)
+              : pairs::build_shared<1, kWaves, kSplits, kStepStride>(
+                    p, s, fullA, fullA ? nullptr : kv_row_of(tA), fullA ? nullptr : ref_row_of(tA),
+                    e0, min(n_rows, e0 + chunk), lsm);
+    const int n_u = nS > sp ? (nS - sp + kSplits - 1) / kSplits : 0;
+    if (n_u > 0) {
+      // Step u: K in slot u%2 of the K slots, V in slot u%2 of the V slots.
+      // Step u issues K of step u+2 and V of step u+1, reads K of step u+1
+      // and V of step u, takes the PV product and row sum of step u-1, S of
+      // step u+1 with the softmax of step u, and ends with the group wait.
+      uint32_t st0 = step_at(0);
+      uint32_t st1 = n_u > 1 ? step_at(1) : kNone | (kNone << 16);
+      uint32_t st2 = n_u > 2 ? step_at(2) : kNone | (kNone << 16);
+      issue_k(st0, kslot0);
+      if (n_u > 1) issue_k(st1, kslot1);
+      issue_v(st0, vslot0);
+      grp_sync();
+      f32x16 sc[2];
+      i32x8 vf[NDB], pprev;
+      int sv_prev = kOne, sv_cur = kOne, ps = kOne;
+      if (q_live) {
+        const uint32_t w0 = unit_word(st0);
+        const int sk = (int)((w0 >> 8) & 0xFFu);
+        sv_cur = (int)((w0 >> 16) & 0xFFu);
+        const int off = unit_off(st0);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
+#pragma unroll
+          for (int cc = 0; cc < NCH; ++cc)
+            sc[kb] = mfma8(frag(kslot0, off, kb * NCH + cc), qf[cc], sc[kb], sk, sq);
+        }
+        const uint32_t me = my_unit(st0);
+        if (me & 0x8000) mask_keys(sc, unit_mask(p, s, me, lane), g);
+        check_max(sc, ps);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) vf[db][j] = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pprev[j] = 0;
+      }
+      grp_sync();
+      // One step with a next step: KR/VR the slots read (K of step u+1, V of
+      // step u), KW/VW the slots refilled (K of step u+2, V of step u+1).
+      auto step = [&](int u, const uint8_t *KR, const uint8_t *VR, uint8_t *KW, uint8_t *VW)
+          __attribute__((always_inline)) {
+        if (u + 2 < n_u) issue_k(st2, KW);
+        issue_v(st1, VW);
+        const uint32_t pend = mysteps[min(u + 3, n_u - 1)];
+        if (q_live) {
+          const uint32_t w1 = unit_word(st1);
+          const int sk1 = (int)((w1 >> 8) & 0xFFu);
+          const int koff = unit_off(st1), voff2 = unit_off(st0);
+          f32x16 sn[2];
+          i32x8 kf[2];
+          i32x8 pf;
+          kf[0] = frag(KR, koff, 0);
+          kf[1] = frag(KR, koff, 1);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < NSLOT; ++i) {
+            // Slots alternate PV (even) and S (odd) while both last.
+            const int pairs_n = NS < NP ? NS : NP;
+            const bool is_s = i < 2 * pairs_n ? (i % 2 == 1) : (NS > NP);
+            const int idx = i < 2 * pairs_n ? i / 2 : i - pairs_n;
+            if (is_s) {
+              const int kb = idx / NCH, cc = idx % NCH;
+              sn[kb] = mfma8(kf[idx % 2], qf[cc], cc == 0 ? f32x16{} : sn[kb], sk1, sq);
+              if (idx + 2 < NS) kf[idx % 2] = frag(KR, koff, idx + 2);
+            } else if (idx < NDB) {
+              o[idx] = mfma8(vf[idx], pprev, o[idx], sv_prev, ps);
+              vf[idx] = frag(VR, voff2, idx);
+            } else {
+              lsum = mfma8(ones, pprev, lsum, kOne, ps);
+            }
+#pragma unroll
+            for (int c = (i * 8 + NSLOT - 1) / NSLOT; c < ((i + 1) * 8 + NSLOT - 1) / NSLOT; ++c)
+              pf[c] = probs4(sc[c / 4], 4 * (c % 4), scale_log2, m_use);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          // Keeps the probabilities and the PV products in the sequence above:
+          // their next uses lie past the branches below, where the compiler
+          // would otherwise move them.
+          keep_here(pf);
+          keep_here(lsum);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) keep_here(o[db]);
+          pprev = pf;
+          sc[0] = sn[0];
+          sc[1] = sn[1];
+          const uint32_t me = my_unit(st1);
+          if (me & 0x8000) mask_keys(sc, unit_mask(p, s, me, lane), g);
+          check_max(sc, ps);
+          sv_prev = sv_cur;
+          sv_cur = (int)((w1 >> 16) & 0xFFu);
+        }
+        grp_sync();
+        st0 = st1;
+        st1 = st2;
+        st2 = __builtin_amdgcn_readfirstlane(pend);
+      };
+      int u = 0;
+      for (; u + 2 < n_u; u += 2) {
+        step(u, kslot1, vslot0, kslot0, vslot1);
+        step(u + 1, kslot0, vslot1, kslot1, vslot0);
+      }
+      if (u + 1 < n_u) {
+        step(u, kslot1, vslot0, kslot0, vslot1);
+        ++u;
+      }
+      // Last step (V in slot u%2): the PV product of step u-1, then the
+      // softmax and PV product of step u.
+      if (q_live) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] = mfma8(vf[db], pprev, o[db], sv_prev, ps);
+        lsum = mfma8(ones, pprev, lsum, kOne, ps);
+        i32x8 pf;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pf[j] = probs4(sc[j / 4], 4 * (j % 4), scale_log2, m_use);
+        const int voff2 = unit_off(st0);
+        const uint8_t *vl = (u % 2 == 0) ? vslot0 : vslot1;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          o[db] = mfma8(frag(vl, voff2, db), pf, o[db], sv_cur, kOne);
+        lsum = mfma8(ones, pf, lsum, kOne, kOne);
+      }
     }
-    if (i < n_mine) unit(ring0, mask, word);
-    const uint64_t mask1 = i + 1 < n_mine ? tile_mask(t1, ok1) : 0ull;
-    sync_slots();
-    bool ok2 = false;
-    int t2 = 0;
-    uint32_t word2 = 0;
-    if (i + 2 < n_mine) {
-      t2 = tile_of(i + 2, ok2);
-      word2 = sc_row[t2];
-      issue(ring0, t2);
-    }
-    if (i + 1 < n_mine) unit(ring1, mask1, word1);
-    sync_slots();
-    t = t2;
-    word = word2;
-    mask = i + 2 < n_mine ? tile_mask(t2, ok2) : 0ull;
+    __syncthreads();                           // lists and slots free for the next chunk
   }
+  if (stalled) fault = 1;
 
-  // Merge the key splits of each query half (the rings are free now:
-  // the last step ended with a barrier).
-  float *osum = reinterpret_cast<float *>(ring0_all);       // [64][D], swizzled
-  float *sm_m = reinterpret_cast<float *>(ring1_all);       // [kSplits][64]
-  float *sm_l = sm_m + kSplits * kTile;
+  // Merge the two key splits of each (tile, query half); the slots are free.
+  float *osum = reinterpret_cast<float *>(tb ? kslot1 : kslot0);   // [64][D], swizzled
+  float *sm_m = reinterpret_cast<float *>(vslot0);                 // [split][tile][64]
+  float *sm_l = sm_m + kSplits * 2 * kTile;
   const int q = qb * 32 + l32;
   if (g == 0) {
-    sm_m[ks * kTile + q] = m_use;
-    sm_l[ks * kTile + q] = lsum[0];                         // every row holds the sum
+    sm_m[(sp * 2 + tb) * kTile + q] = m_use;
+    sm_l[(sp * 2 + tb) * kTile + q] = lsum[0];                     // every row holds the sum
   }
   __syncthreads();
-  float M = sm_m[q];
+  float M = kNegBig;
 #pragma unroll
-  for (int w = 1; w < kSplits; ++w) M = fmaxf(M, sm_m[w * kTile + q]);
+  for (int w = 0; w < kSplits; ++w) M = fmaxf(M, sm_m[(w * 2 + tb) * kTile + q]);
   float L = 0.f;
 #pragma unroll
   for (int w = 0; w < kSplits; ++w)
-    L += sm_l[w * kTile + q] * __builtin_amdgcn_exp2f(sm_m[w * kTile + q] - M);
+    L += sm_l[(w * 2 + tb) * kTile + q] * __builtin_amdgcn_exp2f(sm_m[(w * 2 + tb) * kTile + q] - M);
   const float f = __builtin_amdgcn_exp2f(m_use - M) / L;
   // Element (q, c) of the merged tile sits at q*D + (c ^ (q % 32)).
   for (int turn = 0; turn < kSplits; ++turn) {
-    if (ks == turn) {
+    if (sp == turn) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -301,28 +522,35 @@ void attn_fp8_kernel(Plan p, int total, const uint8_t *__restrict__ q8,
     }
     __syncthreads();
   }
-  const int32_t *qmap = map + (int64_t)tq * kTile;
+  const bool bad = fault != 0;
   bf16_bits *out_bh = out + (int64_t)bh * p.N * D;
-  for (int idx = threadIdx.x; idx < kTile * D / 8; idx += blockDim.x) {
-    const int row = idx / (D / 8), ch = idx % (D / 8);
-    const int32_t tok = qmap[row];
-    if (tok < 0) continue;
-    bf16x8 v8o;
+  for (int t2 = 0; t2 < 2; ++t2) {
+    const int tq = t2 ? tB : tA;
+    if (tq < 0) continue;
+    const int32_t *qmap = map + (int64_t)tq * kTile;
+    const float *os = reinterpret_cast<const float *>(t2 ? kslot1 : kslot0);
+    for (int idx = threadIdx.x; idx < kTile * D / 8; idx += blockDim.x) {
+      const int row = idx / (D / 8), ch = idx % (D / 8);
+      const int32_t tok = qmap[row];
+      if (tok < 0) continue;
+      bf16x8 v8o;
 #pragma unroll
-    for (int e8 = 0; e8 < 8; ++e8)
-      v8o[e8] = (__bf16)osum[row * D + ((ch * 8 + e8) ^ (row % 32))];
-    *reinterpret_cast<bf16x8 *>(out_bh + (int64_t)tok * D + ch * 8) = v8o;
-  }
-  if (lse && threadIdx.x < kTile) {
-    const int qq = threadIdx.x;
-    const int32_t tok = qmap[qq];
-    if (tok >= 0) {
-      float MM = sm_m[qq];
-      for (int w = 1; w < kSplits; ++w) MM = fmaxf(MM, sm_m[w * kTile + qq]);
-      float LL = 0.f;
-      for (int w = 0; w < kSplits; ++w)
-        LL += sm_l[w * kTile + qq] * __builtin_amdgcn_exp2f(sm_m[w * kTile + qq] - MM);
-      lse[(int64_t)bh * p.N + tok] = MM * kLn2 + logf(LL);
+      for (int e8 = 0; e8 < 8; ++e8)
+        v8o[e8] = bad ? (__bf16)NAN : (__bf16)os[row * D + ((ch * 8 + e8) ^ (row % 32))];
+      *reinterpret_cast<bf16x8 *>(out_bh + (int64_t)tok * D + ch * 8) = v8o;
+    }
+    if (lse && threadIdx.x < kTile) {
+      const int qq = threadIdx.x;
+      const int32_t tok = qmap[qq];
+      if (tok >= 0) {
+        float MM = kNegBig;
+        for (int w = 0; w < kSplits; ++w) MM = fmaxf(MM, sm_m[(w * 2 + t2) * kTile + qq]);
+        float LL = 0.f;
+        for (int w = 0; w < kSplits; ++w)
+          LL += sm_l[(w * 2 + t2) * kTile + qq] *
+                __builtin_amdgcn_exp2f(sm_m[(w * 2 + t2) * kTile + qq] - MM);
+        lse[(int64_t)bh * p.N + tok] = bad ? NAN : MM * kLn2 + logf(LL);
+      }
     }
   }
 }
@@ -333,14 +561,14 @@ hipError_t launch_attn_fp8(const Plan &p, const uint8_t *q8, const uint8_t *k8,
                            const uint8_t *v8, const uint8_t *scales, const int32_t *s2t,
                            const int32_t *kv_idx, const int32_t *ref_idx, float scale,
                            void *out, float *lse, hipStream_t stream) {
-  const int total = (int)(p.tiles_per_batch * p.B);
+  const PairGrid gd = pairs::make_grid(p);
   const float sl2 = scale * kLog2e;
   const uint32_t *sw = (const uint32_t *)scales;
   if (p.d == 128)
-    hipLaunchKernelGGL(attn_fp8_kernel<128>, dim3(total), dim3(kThreads), 0, stream, p, total,
+    hipLaunchKernelGGL(attn_fp8_kernel<128>, dim3(gd.total), dim3(kThreads), 0, stream, p, gd,
                        q8, k8, v8, sw, s2t, kv_idx, ref_idx, sl2, (bf16_bits *)out, lse);
   else
-    hipLaunchKernelGGL(attn_fp8_kernel<64>, dim3(total), dim3(kThreads), 0, stream, p, total,
+    hipLaunchKernelGGL(attn_fp8_kernel<64>, dim3(gd.total), dim3(kThreads), 0, stream, p, gd,
                        q8, k8, v8, sw, s2t, kv_idx, ref_idx, sl2, (bf16_bits *)out, lse);
   return hipGetLastError();
 }

@@ -27,9 +27,10 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 # Sources whose text decides each attention kernel's memory traffic.
 KERNEL_SOURCES = {
-    "attn_bf16_kernel": ("csrc/attn_bf16.hip", "csrc/attn_common.h", "csrc/device_common.h"),
-    "attn_fp8_kernel": ("csrc/attn_fp8.hip", "csrc/attn_common.h", "csrc/device_common.h",
-                        "csrc/fp8_layout.h"),
+    "attn_bf16_kernel": ("csrc/attn_bf16.hip", "csrc/attn_pairs.h", "csrc/attn_common.h",
+                         "csrc/device_common.h"),
+    "attn_fp8_kernel": ("csrc/attn_fp8.hip", "csrc/attn_pairs.h", "csrc/attn_common.h",
+                        "csrc/device_common.h", "csrc/fp8_layout.h"),
 }
 
 
