@@ -122,6 +122,29 @@ def make_qkv_f32(w: Workload):
     return q, k, v
 
 
+def rising_exact_arrays(w: Workload, tm):
+    """Inputs on which the attention kernels are exact up to the bf16 store of
+    their output, while their running max rises along every key list.
+    Q and K are small integers: every query has 2 in channels 0..63, every key
+    of tile t has 1 in channels 0..t-1, and channels 64..66 of both are random
+    in {-1, 0, 1}. So q.k = 2t + r with r in [-3, 3]. With softmax scale ln 2,
+    the kernels' logits in log2 units are these integers, every probability is
+    a power of two that E4M3 and bf16 hold exactly, and every key tile lifts
+    the max by about 2, so the max is raised again and again along each key
+    list. V is the seeded bf16 V."""
+    assert tm.n_tiles <= 64 and w.d >= 67
+    rng = np.random.default_rng(11)
+    q, k, v = (np.asarray(a, dtype=np.float32).copy() for a in make_qkv_f32(w))
+    q[...] = 0.0
+    k[...] = 0.0
+    q[..., :64] = 2.0
+    q[..., 64:67] = rng.integers(-1, 2, size=q[..., 64:67].shape)
+    for t in range(tm.n_tiles):
+        k[:, :, tm.tile_tokens(t), :t] = 1.0
+    k[..., 64:67] = rng.integers(-1, 2, size=k[..., 64:67].shape)
+    return q, k, v
+
+
 def problem_of(w: Workload, H=None):
     from block_sparse_video_map_amd import vsa
     return vsa.Problem(w.B, w.H if H is None else H, w.d, w.grid, w.prefix, w.tile_shapes,

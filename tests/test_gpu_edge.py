@@ -162,3 +162,52 @@ def test_deterministic_and_batch_independent():
         c = gs.run_library(w1, arrays=single)
         assert c.layer.out[0].equal(a.layer.out[bi])
         assert c.layer.lse[0].equal(a.layer.lse[bi])
+
+
+def test_bf16_rising_max_exact():
+    """The bf16 kernel raises its running max lazily: a unit whose
+    probability sum passes 2^8 is redone against the raised max. On
+    gpu_support.rising_exact_arrays (integer logits in log2 units with
+    softmax scale ln 2, lifted by about 2 per key tile) every probability is
+    an exact power of two and the max is raised again and again; the outputs
+    must match exact attention to the bf16 rounding of the output, dense and
+    on the GPU's own selection."""
+    import torch
+    from block_sparse_video_map_amd import vsa
+    from workloads.inputs import make_weights
+    w = Workload("edge-rising", "bf16", 2, 2, 128, (5, 16, 20), (40, 300, 24), ((4, 4, 4),),
+                 "mean_gate", 0.75, 2011)
+    tm = oracle.tile_map(*w.grid, w.prefix, w.tile_shapes[0])
+    arrays = gs.rising_exact_arrays(w, tm)
+    scale = float(np.log(2.0))
+    dq, dk, dv = gs.to_device(w, arrays=arrays)
+    wq = torch.from_numpy(make_weights(w)["gate"]).cuda()
+    for sp in (0.0, w.sparsity):
+        gs.log(f"[edge] bf16 rising max, sparsity {sp}")
+        layer = vsa.Layer(gs.problem_of(w), sp, vsa.VSA_SCORE_MEAN_GATE, w.d)
+        layer.forward(dq, dk, dv, wq, None, softmax_scale=scale)
+        torch.cuda.synchronize()
+        sz = layer.sizes
+        for b in range(w.B):
+            for h in range(w.H):
+                if sp == 0.0:
+                    allow = np.ones((tm.n_tiles, tm.n_tiles), dtype=bool)
+                else:
+                    kv = layer.kv_idx[: sz.idx_elems].view(w.B * w.H, sz.max_video_tiles,
+                                                           sz.k_max)
+                    sel = kv[b * w.H + h, :tm.n_video_tiles].cpu().numpy()
+                    allow = oracle.allowed_tiles(
+                        tm, sel[:, :oracle.keep_count(sp, tm.n_video_tiles)])
+                q, k, v = (np.asarray(x[b, h], dtype=np.float64) for x in arrays)
+                want, lse_want = oracle.sparse_attention(q, k, v, tm, allow, scale, None)
+                rows = np.nonzero(~np.isnan(want[:, 0]))[0]
+                got = gs.tensor_f32(layer.out[b, h])[rows]
+                err = np.abs(got - want[rows])
+                bound = 2.0 ** -8 * np.abs(want[rows]) + 1e-4
+                lse_err = float(np.abs(layer.lse[b, h].cpu().numpy()[rows]
+                                       - lse_want[rows]).max())
+                gs.log(f"[edge] bf16 rising max b{b} h{h}: rows {rows.size} "
+                       f"max-abs {err.max():.2e} worst/bound {(err / bound).max():.2f} "
+                       f"lse {lse_err:.2e}")
+                assert np.all(err <= bound)
+                assert lse_err <= 1e-4 * float(np.abs(lse_want[rows]).max()) + 1e-5

@@ -246,42 +246,19 @@ def test_fp8_full_clip_sampled():
 
 
 
-def _rising_exact_arrays(w, tm):
-    """Inputs on which the fp8 kernel is exact up to the bf16 store of its
-    output, while its running max rises again and again along every key list.
-    Q and K are small integers: every query has 2 in channels 0..63, every key
-    of tile t has 1 in channels 0..t-1, and channels 64..66 of both are random
-    in {-1, 0, 1}. So q.k = 2t + r with r in [-3, 3]. With softmax scale ln 2,
-    the kernel's logits in log2 units are these integers, every probability is
-    a power of two that E4M3 holds exactly, and every key tile lifts the max by
-    about 2, so the max is raised every few tiles while the previous tile's
-    probabilities still wait for their PV product. V is the seeded bf16 V."""
-    assert tm.n_tiles <= 64 and w.d >= 67
-    rng = np.random.default_rng(11)
-    q, k, v = (np.asarray(a, dtype=np.float32).copy() for a in gs.make_qkv_f32(w))
-    q[...] = 0.0
-    k[...] = 0.0
-    q[..., :64] = 2.0
-    q[..., 64:67] = rng.integers(-1, 2, size=q[..., 64:67].shape)
-    for t in range(tm.n_tiles):
-        k[:, :, tm.tile_tokens(t), :t] = 1.0
-    k[..., 64:67] = rng.integers(-1, 2, size=k[..., 64:67].shape)
-    return q, k, v
-
-
 @pytest.mark.parametrize("sparsity", [0.0, None], ids=["dense", "sparse"])
 def test_fp8_rising_max_exact(sparsity):
     """The running max is raised with probabilities pending (see
-    _rising_exact_arrays); the outputs must match exact attention over the
-    same E4M3 inputs to the bf16 rounding of the output, and the LSE to
-    float32 accuracy. A wrong rescale of any tile's contribution shows as a
+    gpu_support.rising_exact_arrays); the outputs must match exact attention
+    over the same E4M3 inputs to the bf16 rounding of the output, and the LSE
+    to float32 accuracy. A wrong rescale of any tile's contribution shows as a
     relative error of at least 2^-1 in that tile's weight."""
     import torch
     from block_sparse_video_map_amd import vsa
     from workloads.inputs import make_weights
     w = SMALL["mg-d128"]
     tm = oracle.tile_map(*w.grid, w.prefix, w.tile_shapes[0])
-    arrays = _rising_exact_arrays(w, tm)
+    arrays = gs.rising_exact_arrays(w, tm)
     sp = w.sparsity if sparsity is None else sparsity
     scale = float(np.log(2.0))
     layer = vsa.Layer(gs.problem_of(w), sp, vsa.VSA_SCORE_MEAN_GATE, w.d, fp8=True)
