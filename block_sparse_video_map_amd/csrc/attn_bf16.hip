@@ -6,7 +6,8 @@
 // every step, and each K/V byte a shared step copies serves both tiles
 // (neighbouring tiles share most of their kept tiles). Steps are dealt
 // round-robin to two key splits; a split is four waves (two tiles x two
-// 32-query halves), one per SIMD.
+// 32-query halves), one per SIMD, and the two splits put different query
+// halves on each SIMD.
 //
 // A split's K and V go through two-slot LDS rings filled by direct-to-LDS
 // buffer loads (each of the four waves copies its share; no registers held
@@ -158,7 +159,11 @@ void attn_bf16_kernel(Plan p, PairGrid gd, const bf16_bits *__restrict__ qt,
   const int s = h % p.n_shapes;
   const int bh = b * p.H + h;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
-  const int sp = wave / 4, role = wave % 4;     // split; role = tile*2 + query half
+  // Split 1 takes the roles with the query halves swapped, so that the two
+  // waves of each SIMD (w and w + 4) hold different halves: where a tile's
+  // second half is all pads (its waves skip their products), every SIMD
+  // still has a computing wave.
+  const int sp = wave / 4, role = (wave % 4) ^ sp;   // split; role = tile*2 + query half
   const int tb = role / 2, qb = role % 2;
   const int myT = tb ? tB : tA;
   const int lane = threadIdx.x % 64;

@@ -166,7 +166,11 @@ void attn_fp8_kernel(Plan p, PairGrid gd, const uint8_t *__restrict__ q8,
   const int s = h % p.n_shapes;
   const int bh = b * p.H + h;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
-  const int sp = wave / 4, role = wave % 4;     // split; role = tile*2 + query half
+  // Split 1 takes the roles with the query halves swapped, so that the two
+  // waves of each SIMD (w and w + 4) hold different halves: where a tile's
+  // second half is all pads (its waves skip their products), every SIMD
+  // still has a computing wave.
+  const int sp = wave / 4, role = (wave % 4) ^ sp;   // split; role = tile*2 + query half
   const int tb = role / 2, qb = role % 2;
   const int myT = tb ? tB : tA;
   const int lane = threadIdx.x % 64;
