@@ -340,6 +340,10 @@ BF16_LSE_ABS = 2.0 ** -9 + 1e-4
 # stays within 0.6 of these on the small fp8 test workloads, whose rows see
 # the fewest keys (700 to 2,000; errors shrink as rows see more keys).
 FP8_MAX_ABS, FP8_MEAN_ABS, FP8_LSE_ABS = 5e-2, 4e-3, 2e-2
+# Rows that see few keys (the edge workloads: 192 to 768 keys per row) average
+# the probability rounding over fewer terms; the same CPU model stays within
+# 0.6 of these wider bounds on them (tests/test_fp8_tolerance_model.py).
+FP8_EDGE_MAX_ABS, FP8_EDGE_MEAN_ABS, FP8_EDGE_LSE_ABS = 6e-2, 5e-3, 4e-2
 
 
 def default_scale(d):
