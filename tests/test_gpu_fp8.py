@@ -309,3 +309,25 @@ def test_fp8_edge_workloads(name):
                                                                        tm.n_video_tiles)])
             _compare(w, layer, b, h, allow, tm, label=" edge",
                      tol=(gs.FP8_EDGE_MAX_ABS, gs.FP8_EDGE_MEAN_ABS, gs.FP8_EDGE_LSE_ABS))
+
+
+
+def test_fp8_long_rows_in_chunks():
+    """Workload 5's shapes (3,853 to 4,105 tiles per head, three heads, one
+    per shape): a prefix query tile keeps every key tile, more than one
+    chunk of the kernel's step lists (2,048 tiles), so its rows run over two
+    chunks. Sampled prefix and video query tiles against the oracle on the
+    GPU's own selection."""
+    import dataclasses
+    w = dataclasses.replace(WORKLOADS["5"], H=3)
+    gs.log("[fp8] long rows")
+    layer = _run(w)
+    rng = np.random.default_rng(5)
+    for h in range(w.H):
+        tm = oracle.tile_map(*w.grid, w.prefix, w.tile_shapes[h % len(w.tile_shapes)])
+        assert tm.n_tiles > 2048
+        sel = _selection(w, layer, 0, h, tm.n_video_tiles)
+        allow = oracle.allowed_tiles(tm, sel[:, :oracle.keep_count(w.sparsity, tm.n_video_tiles)])
+        qt = [0, 1, tm.n_prefix_tiles - 1] + sorted(
+            int(tm.n_prefix_tiles + i) for i in rng.choice(tm.n_video_tiles, 4, replace=False))
+        _compare(w, layer, 0, h, allow, tm, query_tiles=qt, label=" long rows")
