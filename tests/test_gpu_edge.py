@@ -211,3 +211,33 @@ def test_bf16_rising_max_exact():
                        f"lse {lse_err:.2e}")
                 assert np.all(err <= bound)
                 assert lse_err <= 1e-4 * float(np.abs(lse_want[rows]).max()) + 1e-5
+
+
+def test_unpaired_long_video_rows():
+    """Video query tiles are paired only while a row's list fits one merged
+    list (1,024 key tiles); the full clip at 30% sparsity keeps 1,235 video
+    tiles per row, so each video query tile runs alone, its list built in
+    chunks. Sampled query tiles against the oracle on the GPU's selection."""
+    import dataclasses
+    from workloads import WORKLOADS
+    w = dataclasses.replace(WORKLOADS["3a"], H=2)
+    sp = 0.3
+    run = gs.run_library(w, sparsity=sp)
+    sz = run.layer.sizes
+    kv = run.layer.kv_idx[: sz.idx_elems].view(w.B * w.H, sz.max_video_tiles, sz.k_max)
+    rng = np.random.default_rng(3)
+    for h in range(w.H):
+        tm = oracle.tile_map(*w.grid, w.prefix, w.tile_shapes[h % len(w.tile_shapes)])
+        k = oracle.keep_count(sp, tm.n_video_tiles)
+        assert tm.n_prefix_tiles + k > 1024
+        tiles = list(range(tm.n_prefix_tiles)) + sorted(
+            int(tm.n_prefix_tiles + i) for i in rng.choice(tm.n_video_tiles, 6, replace=False))
+        gpu_sel = kv[h, : tm.n_video_tiles, :k].cpu().numpy()
+        ro, _ = gs.oracle_head(w, h, sparsity=sp, query_tiles=tiles, kv_video=gpu_sel)
+        rows = np.concatenate([tm.tile_tokens(t) for t in tiles])
+        got = gs.tensor_f32(run.layer.out[0, h])[rows]
+        mx, mean = gs.bf16_stats(got, ro["out"][rows])
+        lse_err = float(np.abs(run.layer.lse[0, h].cpu().numpy()[rows] - ro["lse"][rows]).max())
+        gs.log(f"[edge] unpaired rows h{h}: max-abs {mx:.2e} mean-abs {mean:.2e} lse {lse_err:.2e}")
+        assert mx <= gs.BF16_MAX_ABS and mean <= gs.BF16_MEAN_ABS
+        assert lse_err <= gs.BF16_LSE_ABS

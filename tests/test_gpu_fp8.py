@@ -331,3 +331,23 @@ def test_fp8_long_rows_in_chunks():
         qt = [0, 1, tm.n_prefix_tiles - 1] + sorted(
             int(tm.n_prefix_tiles + i) for i in rng.choice(tm.n_video_tiles, 4, replace=False))
         _compare(w, layer, 0, h, allow, tm, query_tiles=qt, label=" long rows")
+
+
+
+def test_fp8_unpaired_long_video_rows():
+    """The fp8 kernel's unpaired video rows: the full clip at 30% sparsity
+    keeps 1,235 video tiles per row, past the 1,024 of a merged pair list."""
+    import dataclasses
+    w = dataclasses.replace(WORKLOADS["3a"], H=2)
+    sp = 0.3
+    layer = _run(w, sparsity=sp)
+    rng = np.random.default_rng(3)
+    for h in range(w.H):
+        tm = oracle.tile_map(*w.grid, w.prefix, w.tile_shapes[h % len(w.tile_shapes)])
+        k = oracle.keep_count(sp, tm.n_video_tiles)
+        assert tm.n_prefix_tiles + k > 1024
+        sel = _selection(w, layer, 0, h, tm.n_video_tiles)
+        allow = oracle.allowed_tiles(tm, sel[:, :k])
+        qt = list(range(tm.n_prefix_tiles)) + sorted(
+            int(tm.n_prefix_tiles + i) for i in rng.choice(tm.n_video_tiles, 6, replace=False))
+        _compare(w, layer, 0, h, allow, tm, query_tiles=qt, label=" unpaired")
