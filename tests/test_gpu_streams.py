@@ -28,15 +28,18 @@ def _layer(w, fp8, fused=False):
     return layer, gs.to_device(w), weights
 
 
-@pytest.mark.parametrize("fp8,fused", [(False, False), (True, False), (False, True)],
-                         ids=["bf16", "fp8", "bf16-fused-select"])
-def test_two_streams_match_sequential_runs(fp8, fused):
+@pytest.mark.parametrize("fp8_a,fp8_b,fused",
+                         [(False, False, False), (True, True, False), (False, False, True),
+                          (False, True, False)],
+                         ids=["bf16", "fp8", "bf16-fused-select", "bf16-beside-fp8"])
+def test_two_streams_match_sequential_runs(fp8_a, fp8_b, fused):
     """The fused case also guards the bf16 attention kernel against stale LDS:
     its V rings must not feed bytes another kernel left there (possibly NaN
-    patterns) into the products of a step without a unit."""
+    patterns) into the products of a step without a unit. The mixed case runs
+    the two attention kernels beside each other."""
     import torch
-    la, ia, wa = _layer(A, fp8, fused)
-    lb, ib, wb = _layer(B, fp8, fused)
+    la, ia, wa = _layer(A, fp8_a, fused)
+    lb, ib, wb = _layer(B, fp8_b, fused)
     la.forward(*ia, *wa)
     lb.forward(*ib, *wb)
     torch.cuda.synchronize()
@@ -52,6 +55,6 @@ def test_two_streams_match_sequential_runs(fp8, fused):
             lb.forward(*ib, *wb)
     torch.cuda.synchronize()
     got = [la.out, la.lse, lb.out, lb.lse]
-    gs.log(f"[streams] fp8={fp8} fused={fused}: comparing {len(got)} buffers")
+    gs.log(f"[streams] fp8={fp8_a},{fp8_b} fused={fused}: comparing {len(got)} buffers")
     for r, g in zip(ref, got):
         assert torch.equal(r, g)
