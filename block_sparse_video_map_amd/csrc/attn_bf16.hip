@@ -259,8 +259,14 @@ void attn_bf16_kernel(Plan p, PairGrid gd, const bf16_bits *__restrict__ qt,
   // copy the two halves of K, roles 2 and 3 the two halves of V. Separate
   // units: role 0 copies A's K, role 1 A's V, role 2 B's K, role 3 B's V
   // (A's unit at offset 0 of the slot, B's at UNIT).
+  // The split's offset into the slot arrays goes through an empty asm, so
+  // that each copy's LDS base is one scalar add per step. Otherwise the
+  // compiler keeps one base per slot, role and block live across the loop;
+  // they spill, and every step reads them back with VALU instructions.
   auto issue_k = [&](uint32_t st, bf16_bits *slot_all) __attribute__((always_inline)) {
-    bf16_bits *dst = slot_all + sp * SLOT;
+    int sbase = sp * SLOT;
+    asm volatile("" : "+s"(sbase));
+    bf16_bits *dst = slot_all + sbase;
     const uint32_t eA = st & 0xFFFFu, eB = st >> 16;
     if (eA == eB) {
       if (role < 2 && eA != kNone) {
@@ -284,7 +290,9 @@ void attn_bf16_kernel(Plan p, PairGrid gd, const bf16_bits *__restrict__ qt,
     }
   };
   auto issue_v = [&](uint32_t st, bf16_bits *slot_all) __attribute__((always_inline)) {
-    bf16_bits *dst = slot_all + sp * SLOT;
+    int sbase = sp * SLOT;
+    asm volatile("" : "+s"(sbase));
+    bf16_bits *dst = slot_all + sbase;
     const uint32_t eA = st & 0xFFFFu, eB = st >> 16;
     if (eA == eB) {
       if (role >= 2 && eA != kNone) {
