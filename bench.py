@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="with --profile-attn-only: also run one plain device copy of this "
                          "many MiB (reference for the memory-traffic counters)")
+    ap.add_argument("--overlap-probe", action="store_true",
+                    help="only measure how exponentials share a SIMD with fp8 products "
+                         "(vsa_mfma_probe kinds 1-3) and print one JSON line")
     return ap.parse_args()
 
 
@@ -421,6 +424,32 @@ def cpu_baseline(wname: str, budget_s: float):
             "nproc": os.cpu_count(), "blas_threads": blas_threads()}
 
 
+def overlap_probe(iters: int = 20000) -> dict:
+    """Shader cycles per trip of vsa_mfma_probe's fp8 kinds (median over
+    workgroups of the span of their waves' loops), one workgroup per CU:
+    four fp8 MFMAs per trip in one wave per SIMD (kind 1) or two (kind 2),
+    two waves that each add 16 exponentials (kind 3), or one wave of products
+    beside one that only runs the 16 exponentials (kind 4)."""
+    import torch
+    from block_sparse_video_map_amd import vsa
+    cu, _, _ = vsa.vsa_device_clocks()
+    rows = (("products, one wave per SIMD", 1, cu),
+            ("products, two waves per SIMD", 2, cu),
+            ("products + 16 exp in each wave, two waves per SIMD", 3, cu),
+            ("products wave beside an exp wave on each SIMD", 4, cu))
+    out = {"iters": iters, "mfma_cycles_per_trip_alone": 4 * 64, "rows": []}
+    for name, kind, n_wg in rows:
+        ticks = torch.zeros(4 * n_wg, dtype=torch.int64, device="cuda")
+        vsa.vsa_mfma_probe(kind, iters, n_wg)        # warm-up
+        vsa.vsa_mfma_probe(kind, iters, n_wg, ticks)
+        torch.cuda.synchronize()
+        tk = ticks.view(n_wg, 4).cpu().double()
+        cyc = float(((tk[:, 1] - tk[:, 0]) / iters).median())
+        out["rows"].append({"case": name, "kind": kind, "workgroups": n_wg,
+                            "cycles_per_trip": round(cyc, 1)})
+    return out
+
+
 def measured_peak(reps: int = 5) -> dict:
     """The matrix-core rate the chip sustains under a pure MFMA load (bf16
     and fp8), and the clocks behind it: the engine clock the runtime reports
@@ -511,6 +540,9 @@ def main():
     from block_sparse_video_map_amd import vsa
     from workloads import WORKLOADS
 
+    if a.overlap_probe:
+        print(json.dumps(overlap_probe()), flush=True)
+        return
     w = WORKLOADS[a.workload]
     if a.fp8 and not a.profile_attn_only:
         print("--fp8 only applies to --profile-attn-only (the headline is the bf16 path)",

@@ -416,7 +416,7 @@ VSA_API int vsa_device_clocks(int32_t *cu_count, int32_t *clock_khz, int32_t *wa
 
 VSA_API int vsa_mfma_probe(int32_t kind, int32_t iters, int32_t n_workgroups, uint64_t *ticks,
                            void *stream) {
-  if (kind != 0 && kind != 1) return VSA_ERR_INVALID_ARG;
+  if (kind < 0 || kind > 4) return VSA_ERR_INVALID_ARG;
   if (iters < 1 || n_workgroups < 1) return VSA_ERR_INVALID_ARG;
   if (iters > (1 << 22) || n_workgroups > (1 << 16)) return VSA_ERR_SIZE;
   if ((uintptr_t)ticks & 7u) return VSA_ERR_INVALID_ARG;

@@ -536,7 +536,10 @@ def vsa_sparse_attn_fwd_fp8(prob: Problem, q8, k8, v8, scales, slot_to_token, kv
 
 # ------------------------------------------------------- measurement aids
 
-MFMA_PROBE_FLOPS = (32 * 32 * 16 * 2, 32 * 32 * 64 * 2)   # per MFMA: bf16, fp8
+# flop per MFMA of each probe kind: bf16, then fp8 (kinds 1-4), and MFMAs per
+# workgroup and trip
+MFMA_PROBE_FLOPS = (32 * 32 * 16 * 2,) + (32 * 32 * 64 * 2,) * 4
+MFMA_PROBE_PER_TRIP = (16, 16, 32, 32, 16)
 
 
 def vsa_device_clocks():
@@ -549,14 +552,16 @@ def vsa_device_clocks():
 
 
 def vsa_mfma_probe(kind: int, iters: int, n_workgroups: int, ticks=None, stream=None) -> int:
-    """Enqueues the matrix-core load (kind 0 bf16, 1 fp8); ticks is an int64
-    device tensor of 4 * n_workgroups counters or None. Returns the flops
-    the launch performs."""
+    """Enqueues the matrix-core load (kind 0 bf16, 1 fp8; in 8-wave
+    workgroups: 2 fp8, 3 fp8 with exponentials in the same waves, 4 fp8
+    beside waves of exponentials); ticks is an int64 device tensor of
+    4 * n_workgroups counters or None. Returns the flops the launch
+    performs."""
     import torch
     _need(ticks, 4 * n_workgroups, torch.int64, "ticks")
     _check("vsa_mfma_probe", lib().vsa_mfma_probe(int(kind), int(iters), int(n_workgroups),
                                                   _ptr(ticks), _stream(stream)))
-    return n_workgroups * 16 * iters * MFMA_PROBE_FLOPS[kind]
+    return n_workgroups * MFMA_PROBE_PER_TRIP[kind] * iters * MFMA_PROBE_FLOPS[kind]
 
 
 # ---------------------------------------------------------- whole-layer helper

@@ -485,12 +485,17 @@ VSA_API int vsa_sparse_attn_fwd_fp8(const vsa_problem *prob, const void *q8, con
  * waves); every wave runs `iters` trips of 4 independent MFMAs:
  *   kind 0: bf16 32x32x16   (32768 flop each, the bf16 attention's type)
  *   kind 1: E4M3 32x32x64 with unit block scales (131072 flop each)
- * so one launch performs n_workgroups * 16 * iters MFMAs. ticks: device
- * uint64 [n_workgroups][4] or NULL; wave 0 of workgroup w writes the shader
- * tick counter before and after its loop (ticks[w][0], [1]) and the
- * real-time counter likewise ([2], [3]), 8-byte aligned. Nothing else is
- * written. 1 <= iters <= 2^22 and 1 <= n_workgroups <= 2^16
- * (VSA_ERR_SIZE above, VSA_ERR_INVALID_ARG below or for another kind).
+ * so one launch performs n_workgroups * 16 * iters MFMAs. Kinds 2-4 run
+ * workgroups of 512 threads (8 waves, two on every SIMD) of kind 1's trips:
+ *   kind 2: every wave runs the trips (32 MFMAs per workgroup and trip)
+ *   kind 3: every wave adds 16 exponentials (v_exp_f32) per trip (32 MFMAs)
+ *   kind 4: waves 0-3 run the trips, waves 4-7 only the 16 exponentials per
+ *           trip (16 MFMAs per workgroup and trip). ticks: device
+ * uint64 [n_workgroups][4] or NULL, 8-byte aligned; workgroup w writes the
+ * span of its waves' loops on the shader tick counter (earliest start
+ * ticks[w][0], latest end [1]) and on the real-time counter ([2], [3]).
+ * Nothing else is written. 1 <= iters <= 2^22 and 1 <= n_workgroups <= 2^16
+ * (VSA_ERR_SIZE above, VSA_ERR_INVALID_ARG below or for a kind outside 0..4).
  */
 VSA_API int vsa_device_clocks(int32_t *cu_count, int32_t *clock_khz, int32_t *wall_khz);
 VSA_API int vsa_mfma_probe(int32_t kind, int32_t iters, int32_t n_workgroups, uint64_t *ticks,

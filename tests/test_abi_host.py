@@ -377,7 +377,8 @@ def test_fused_map_fp8_rejects_before_any_launch():
 
 def test_mfma_probe_rejects_before_any_launch():
     L = vsa.lib()
-    assert L.vsa_mfma_probe(2, 1, 1, None, None) == vsa.VSA_ERR_INVALID_ARG
+    assert L.vsa_mfma_probe(5, 1, 1, None, None) == vsa.VSA_ERR_INVALID_ARG
+    assert L.vsa_mfma_probe(-1, 1, 1, None, None) == vsa.VSA_ERR_INVALID_ARG
     assert L.vsa_mfma_probe(0, 0, 1, None, None) == vsa.VSA_ERR_INVALID_ARG
     assert L.vsa_mfma_probe(1, 1, 0, None, None) == vsa.VSA_ERR_INVALID_ARG
     assert L.vsa_mfma_probe(0, (1 << 22) + 1, 1, None, None) == vsa.VSA_ERR_SIZE
@@ -388,7 +389,9 @@ def test_mfma_probe_rejects_before_any_launch():
 
 def test_mfma_probe_flop_count():
     # one 32x32xK product is 2*32*32*K flops; a workgroup has 4 waves of 4 chains
-    assert vsa.MFMA_PROBE_FLOPS == (2 * 32 * 32 * 16, 2 * 32 * 32 * 64)
+    # (kinds 2-4: 8 waves, of which kind 4 runs the products in 4)
+    assert vsa.MFMA_PROBE_FLOPS == (2 * 32 * 32 * 16,) + (2 * 32 * 32 * 64,) * 4
+    assert vsa.MFMA_PROBE_PER_TRIP == (16, 16, 32, 32, 16)
 
 
 # ------------------------------------------------- random geometries (planner)

@@ -9,7 +9,8 @@ from tests import gpu_support as gs
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("kind", [0, 1], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("kind", [0, 1, 2, 3, 4],
+                         ids=["bf16", "fp8", "fp8-8waves", "fp8-exp", "fp8-beside-exp"])
 def test_probe_rate_and_counters(kind):
     import torch
     from block_sparse_video_map_amd import vsa
@@ -40,4 +41,4 @@ def test_probe_null_ticks_and_errors():
     vsa.vsa_mfma_probe(0, 1, 1)
     torch.cuda.synchronize()
     with pytest.raises(vsa.VSAError):
-        vsa.vsa_mfma_probe(3, 1, 1)
+        vsa.vsa_mfma_probe(5, 1, 1)
