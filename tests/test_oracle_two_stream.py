@@ -6,8 +6,6 @@ query row stays dense ("BSAI-ComfyUI-VedaSparse" README, section "v3.4.2
 Vendored Official Veda (Pull-and-Go)", R2VA predictor row).
 """
 
-import itertools
-
 import numpy as np
 import pytest
 
