@@ -181,6 +181,24 @@ def run_library(w: Workload, sparsity=None, stages=("map", "score", "select", "a
     return GpuRun(w, prob, layer, q, k, v, wq, wk)
 
 
+def assert_same_without_lse(layer, label=""):
+    """Attention called without an LSE buffer, the form the benchmark times,
+    writes the same output bit for bit as the call that returned one (the
+    layer's current output, checked against the oracle by the caller)."""
+    import torch
+    out, lse = layer.out, layer.lse
+    try:
+        layer.out = torch.full_like(out, float("nan"))
+        layer.lse = None
+        layer.attend()
+        torch.cuda.synchronize()
+        same = torch.equal(layer.out.view(torch.uint8), out.view(torch.uint8))
+    finally:
+        layer.out, layer.lse = out, lse
+    log(f"[no-lse]{label}: output {'identical' if same else 'DIFFERS'} without the LSE buffer")
+    assert same
+
+
 def fused_kv(run: GpuRun, sparsity=None):
     """kv_idx from vsa_tile_select (pooling, scores and top-k in one call) on
     the run's tiled copies, or None when the call does not take the problem."""

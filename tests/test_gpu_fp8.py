@@ -242,6 +242,7 @@ def test_fp8_full_clip_sampled():
         qt = list(range(tm.n_prefix_tiles)) + sorted(
             int(tm.n_prefix_tiles + i) for i in rng.choice(tm.n_video_tiles, 12, replace=False))
         _compare(w, layer, 0, h, allow, tm, query_tiles=qt, label=" sampled")
+    gs.assert_same_without_lse(layer, " fp8 full clip")
     del layer
     torch.cuda.empty_cache()
 

@@ -183,3 +183,7 @@ def test_attention_matches_oracle(run):
         else:
             assert mx <= gs.BF16_MAX_ABS and mean <= gs.BF16_MEAN_ABS
             assert lse_err <= gs.BF16_LSE_ABS
+
+
+def test_attention_without_lse_bit_identical(run):
+    gs.assert_same_without_lse(run.layer, f" workload {run.name}")

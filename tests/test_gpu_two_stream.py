@@ -103,3 +103,4 @@ def test_two_stream_headline_shape():
         npt = 73
         qt = list(range(npt)) + list(npt + rng.choice(1764, 16, replace=False))
         _check_head(w, r, 0, h, ref, query_tiles=qt)
+    gs.assert_same_without_lse(r.layer, " two-stream 3b")
