@@ -279,7 +279,7 @@ void attn_bf16_kernel(Plan p, PairGrid gd, const bf16_bits *__restrict__ qt,
           copy4k(rk, (lds_ptr_t)dst, voff, tile * TB + kb * UB);
       }
     } else if (role == 0 || role == 2) {
-      const uint32_t e = role == 0 ? eA : eB;
+      const uint32_t e = (st >> (8 * role)) & 0xFFFFu;
       if (e != kNone) {
         const int tile = (int)((e & 0x7FFF) >> 1), kb = (int)(e & 1);
         bf16_bits *d2 = dst + (role / 2) * UNIT;
@@ -304,7 +304,7 @@ void attn_bf16_kernel(Plan p, PairGrid gd, const bf16_bits *__restrict__ qt,
         }
       }
     } else if (role == 1 || role == 3) {
-      const uint32_t e = role == 1 ? eA : eB;
+      const uint32_t e = (st >> (8 * (role - 1))) & 0xFFFFu;
       if (e != kNone) {
         const int tile = (int)((e & 0x7FFF) >> 1), kb = (int)(e & 1);
         bf16_bits *d2 = dst + (role / 2) * UNIT;

@@ -290,7 +290,7 @@ void attn_fp8_kernel(Plan p, PairGrid gd, const uint8_t *__restrict__ q8,
                             tile * TB + role * (TB / 2));
       }
     } else if (role == 0 || role == 2) {
-      const uint32_t e = role == 0 ? eA : eB;
+      const uint32_t e = (st >> (8 * role)) & 0xFFFFu;
       if (e != kNone) {
         const int tile = (int)(e & 0x7FFF);
         uint8_t *d2 = dst + (role / 2) * TB;
@@ -310,7 +310,7 @@ void attn_fp8_kernel(Plan p, PairGrid gd, const uint8_t *__restrict__ q8,
                             tile * TB + (role - 2) * (TB / 2));
       }
     } else if (role == 1 || role == 3) {
-      const uint32_t e = role == 1 ? eA : eB;
+      const uint32_t e = (st >> (8 * (role - 1))) & 0xFFFFu;
       if (e != kNone) {
         const int tile = (int)(e & 0x7FFF);
         uint8_t *d2 = dst + (role / 2) * TB;

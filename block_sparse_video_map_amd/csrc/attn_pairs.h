@@ -78,13 +78,16 @@ __device__ inline int unit_real(const Plan &p, int s, int tile, int kb) {
   const int pt = p.shape[s][0], ph = p.shape[s][1], pw = p.shape[s][2];
   const int rt = min(pt, p.T - ti * pt), rh = min(ph, p.Hv - hi * ph), rw = min(pw, p.Wv - wi * pw);
   if (rt == pt && rh == ph && rw == pw) return 32;
-  int n = 0;
-  for (int j = 0; j < 32; ++j) {
-    const int slot = kb * 32 + j;
-    const int a = slot / (ph * pw), bb = (slot / pw) % ph, c = slot % pw;
-    n += (a < rt) & (bb < rh) & (c < rw);
-  }
-  return n;
+  // Slot (a*ph + b)*pw + c is real when a < rt, b < rh and c < rw. The
+  // extents are powers of two (their product is 64), so a half of the tile
+  // is a whole range along one axis: the a-planes [kb*pt/2, (kb+1)*pt/2)
+  // when a plane holds at most 32 slots, else (pt = 1) the b-rows
+  // [kb*ph/2, (kb+1)*ph/2) when a row holds at most 32, else (ph = 1) the
+  // columns [kb*32, kb*32 + 32).
+  auto overlap = [](int lo, int len, int r) { return max(0, min(lo + len, r) - lo); };
+  if (ph * pw <= 32) return overlap(kb * (pt / 2), pt / 2, rt) * rh * rw;
+  if (pw <= 32) return overlap(kb * (ph / 2), ph / 2, rh) * rw;
+  return overlap(kb * 32, 32, rw);
 }
 
 // Query tiles tA, tB (tB < 0: none) of workgroup blockIdx.x. Workgroups
